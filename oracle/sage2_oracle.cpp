@@ -1,0 +1,449 @@
+// CPU oracle for the SageAttention2 forward pass.
+//
+// TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU-baseline leg of the
+// benchmark load this library. The GPU library never links, calls or includes it, and the two share
+// no code: this file has its own codec, its own group map and its own arithmetic.
+//
+// Sources (cited by page title and section; no other document is relied on):
+//   [ABS]  PMLR vol. 267 page "SageAttention2: Efficient Attention with Thorough Outlier Smoothing
+//          and Per-thread INT4 Quantization", Abstract: Q and K are quantized to INT4 at thread-level
+//          granularity, P~ and V to FP8; Q is smoothed; P~V uses a two-level accumulation.
+//   [REC]  research record "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and
+//          Per-thread INT4 Quantization", paragraph "Three components": Q smoothing, per-thread INT4
+//          scales held in registers, two-level accumulation for the FP8 PV product.
+//   [VIZ]  visual companion "SageAttention2 and Fast Exact INT4 Attention", sections "Numerical
+//          Repair Stack", "Channel Outlier Smoothing", "Per-Thread INT4 Geometry",
+//          "Implementation envelope".
+//   [EP]   episode page "SageAttention2 and Fast Exact INT4 Attention", description (exact attention
+//          rule kept; smoothing of K; lineage from FlashAttention-2's online softmax).
+//
+// The pages name the steps but give no formulas, block sizes, rounding rules or FP8 flavour. Each
+// reading taken here is listed, with its reason, in the repository's design notes; the short form is
+// repeated next to the code that implements it.
+//
+// Precision: floating point that only feeds a real-valued result is carried in fp64. Floating point
+// that decides an integer (an INT4 code, an FP8 code) is evaluated in the precision the GPU kernel
+// uses (f32, IEEE round-to-nearest-even, no contraction) so that both sides take the same decision.
+// Build with -ffp-contract=off.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <functional>
+#include <limits>
+#include <thread>
+#include <vector>
+
+namespace {
+
+constexpr int kQBlock = 128;   // Q smoothing block: tokens sharing one mean (reading: 128, aligned to sequence start)
+constexpr int kKChunk = 128;   // K mean: fp64 partial sums over 128-token chunks, then chunks in order
+constexpr float kLog2e = 1.44269504088896340736f;      // log2(e) rounded to f32
+constexpr float kLog2_448 = 8.80735492205760410750f;   // log2(448) rounded to f32
+constexpr double kInf = std::numeric_limits<double>::infinity();
+constexpr float kInfF = std::numeric_limits<float>::infinity();
+
+void parallel_for(int n, int nthreads, const std::function<void(int)>& fn) {
+  if (nthreads <= 1 || n <= 1) {
+    for (int i = 0; i < n; ++i) fn(i);
+    return;
+  }
+  nthreads = std::min(nthreads, n);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < nthreads; ++t)
+    pool.emplace_back([&, t] {
+      for (int i = t; i < n; i += nthreads) fn(i);
+    });
+  for (auto& th : pool) th.join();
+}
+
+int resolve_threads(int n) {
+  if (n > 0) return n;
+  unsigned hc = std::thread::hardware_concurrency();
+  return hc ? (int)hc : 1;
+}
+
+float resolve_scale(float sm_scale, int d) {
+  // Default softmax scale 1/sqrt(d) in f32 (standard attention scaling; [ABS] keeps the dense rule).
+  return sm_scale != 0.0f ? sm_scale : 1.0f / std::sqrt((float)d);
+}
+
+// ---- OCP FP8 E4M3 ("e4m3fn") codec, written from the format definition -------------------------
+// 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits. Exponent field 0 holds subnormals
+// m * 2^-9. No infinities; S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+double e4m3_decode(uint8_t c) {
+  const double sign = (c & 0x80) ? -1.0 : 1.0;
+  const int e = (c >> 3) & 0xF;
+  const int m = c & 7;
+  if (e == 15 && m == 7) return std::numeric_limits<double>::quiet_NaN();
+  if (e == 0) return sign * std::ldexp((double)m, -9);
+  return sign * std::ldexp(1.0 + m / 8.0, e - 7);
+}
+
+// Round to nearest, ties to even mantissa; magnitudes at or above 448 saturate to 448 (reading: the
+// pages do not say how out-of-range values are handled; every value the method encodes is <= 448
+// up to f32 rounding, so saturation only guards the last ulp). The sign of zero is kept.
+uint8_t e4m3_encode(double x) {
+  if (std::isnan(x)) return 0x7F;
+  const uint8_t sign = std::signbit(x) ? 0x80 : 0x00;
+  const double a = std::fabs(x);
+  if (a >= 448.0) return sign | 0x7E;
+  // grid spacing at a: 2^-9 below the smallest normal 2^-6, else 2^(floor(log2 a) - 3)
+  const double step = (a < 0x1p-6) ? 0x1p-9 : std::ldexp(1.0, std::ilogb(a) - 3);
+  const double r = std::nearbyint(a / step);  // default rounding mode: ties to even
+  const double v = r * step;
+  if (v >= 448.0) return sign | 0x7E;
+  if (v < 0x1p-6) return sign | (uint8_t)r;  // subnormal, or zero
+  const int e = std::ilogb(v);
+  const int m = (int)std::lround(std::ldexp(v, 3 - e)) - 8;
+  // v == 2^-6 exactly also lands here with e = -6, m = 0.
+  return sign | (uint8_t)(((e + 7) << 3) | m);
+}
+
+// ---- INT4 symmetric quantizer (reading: grid [-7, 7], scale = amax / 7) ---------------------------
+// [ABS]/[REC]: Q and K are quantized to INT4, one scale per thread-owned group. Codes are
+// round-to-nearest-even of x * (7 / amax) evaluated in f32; an all-zero group gets scale 0.
+struct Int4Scale { float s, inv; };
+
+Int4Scale int4_scale(float amax) {
+  if (amax == 0.0f) return {0.0f, 0.0f};
+  return {amax / 7.0f, 7.0f / amax};
+}
+
+int8_t int4_code(float x, float inv) {
+  const float y = x * inv;  // one f32 rounding
+  float r = std::nearbyint(y);
+  r = std::min(7.0f, std::max(-7.0f, r));
+  return (int8_t)r;
+}
+
+// K scale group of key j (reading of "per-thread" on the gfx950 32x32 MFMA, where a lane half owns
+// the keys of a 32-key tile whose in-tile index has bit 2 equal to the half index): two groups of 16
+// keys per 32-key tile.
+inline int kgroup(int j) { return 2 * (j / 32) + ((j >> 2) & 1); }
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+enum {
+  ORC_NO_K_SMOOTH = 1,  // ablation: skip the K mean subtraction
+  ORC_NO_Q_SMOOTH = 2,  // ablation: skip the Q block mean subtraction (and so the correction term)
+};
+enum {
+  ORC_ATTN_NO_P8 = 1,   // keep P~ unquantized (used to compare the online form with a two-pass form)
+};
+
+double orc_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
+uint8_t orc_e4m3_encode(double x) { return e4m3_encode(x); }
+int orc_kgroup(int j) { return kgroup(j); }
+
+// Smoothing and quantization for one sequence.
+//   q  : [Hq][Lq][d]   f32 (exact widening of the fp16/bf16 input)
+//   k,v: [Hkv][Lkv][d] f32
+// Outputs (all caller-allocated):
+//   kbar  [Hkv][d] f32          per-channel token mean of K                     ([VIZ] Channel Outlier Smoothing)
+//   qbar  [Hq][nqb][d] f32      per-128-token-block mean of Q, nqb = ceil(Lq/128) ([ABS], [REC] Q smoothing)
+//   qcode [Hq][Lq][d] i8, sq [Hq][Lq] f32       INT4 codes of Q - qbar, one scale per token
+//   kcode [Hkv][Lkv][d] i8, sk [Hkv][2*ceil(Lkv/32)] f32   INT4 codes of K - kbar, one scale per 16-key group
+//   v8    [Hkv][Lkv][d] u8, sv [Hkv][d] f32     FP8 e4m3 codes of V scaled per channel to amax 448 ([ABS])
+//   delta [Hq][nqb][Lkv] f32 or NULL            correction q̄·k̃_j in base-2 logit units (see below)
+// Returns 0 on success, -1 on a bad argument.
+int orc_quantize(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int flags,
+                 const float* q, const float* k, const float* v,
+                 float* kbar, float* qbar, int8_t* qcode, float* sq, int8_t* kcode, float* sk,
+                 uint8_t* v8, float* sv, float* delta, int nthreads) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lq <= 0 || Lkv <= 0 || d <= 0) return -1;
+  nthreads = resolve_threads(nthreads);
+  const int nqb = ceil_div(Lq, kQBlock);
+  const int ngk = 2 * ceil_div(Lkv, 32);
+  const float L = resolve_scale(sm_scale, d) * kLog2e;  // logits are carried in base-2 units
+  std::vector<float> ktil((size_t)Hkv * Lkv * d);
+
+  parallel_for(Hkv, nthreads, [&](int g) {
+    const float* K = k + (size_t)g * Lkv * d;
+    const float* V = v + (size_t)g * Lkv * d;
+    float* KT = ktil.data() + (size_t)g * Lkv * d;
+    // 1. K mean over all Lkv tokens of the sequence (reading: also future tokens under a causal
+    //    mask; any per-channel shift of K adds a per-row constant to the logits, which softmax
+    //    ignores). fp64 sums over 128-token chunks, then the chunk sums in order.
+    for (int c = 0; c < d; ++c) {
+      double total = 0.0;
+      for (int j0 = 0; j0 < Lkv; j0 += kKChunk) {
+        double part = 0.0;
+        for (int j = j0; j < std::min(Lkv, j0 + kKChunk); ++j) part += (double)K[(size_t)j * d + c];
+        total += part;
+      }
+      kbar[(size_t)g * d + c] = (flags & ORC_NO_K_SMOOTH) ? 0.0f : (float)(total / (double)Lkv);
+    }
+    for (int j = 0; j < Lkv; ++j)
+      for (int c = 0; c < d; ++c)
+        KT[(size_t)j * d + c] = K[(size_t)j * d + c] - kbar[(size_t)g * d + c];
+    // 3. K codes: one scale per group of 16 keys (kgroup), shared by all channels.
+    //    A group's keys all lie in one 32-key tile, so only that tile is scanned for members.
+    for (int grp = 0; grp < ngk; ++grp) {
+      const int j0 = 32 * (grp / 2), j1 = std::min(Lkv, j0 + 32);
+      float amax = 0.0f;
+      for (int j = j0; j < j1; ++j)
+        if (kgroup(j) == grp)
+          for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(KT[(size_t)j * d + c]));
+      const Int4Scale s = int4_scale(amax);
+      sk[(size_t)g * ngk + grp] = s.s;
+      for (int j = j0; j < j1; ++j)
+        if (kgroup(j) == grp)
+          for (int c = 0; c < d; ++c)
+            kcode[((size_t)g * Lkv + j) * d + c] = int4_code(KT[(size_t)j * d + c], s.inv);
+    }
+    // 4. V: per channel, scale so that the channel's amax maps to 448, then encode e4m3.
+    for (int c = 0; c < d; ++c) {
+      float amax = 0.0f;
+      for (int j = 0; j < Lkv; ++j) amax = std::max(amax, std::fabs(V[(size_t)j * d + c]));
+      const float s = amax == 0.0f ? 0.0f : amax / 448.0f;
+      const float inv = amax == 0.0f ? 0.0f : 448.0f / amax;
+      sv[(size_t)g * d + c] = s;
+      for (int j = 0; j < Lkv; ++j) {
+        const float y = V[(size_t)j * d + c] * inv;
+        v8[((size_t)g * Lkv + j) * d + c] = e4m3_encode((double)y);
+      }
+    }
+  });
+
+  parallel_for(Hq, nthreads, [&](int h) {
+    const float* Q = q + (size_t)h * Lq * d;
+    const int g = h / (Hq / Hkv);  // consecutive q heads share a kv head
+    const float* KT = ktil.data() + (size_t)g * Lkv * d;
+    std::vector<float> qt(d);
+    for (int b = 0; b < nqb; ++b) {
+      const int i0 = b * kQBlock, i1 = std::min(Lq, i0 + kQBlock);
+      float* qb = qbar + ((size_t)h * nqb + b) * d;
+      // 2. Q block mean over the block's valid rows (fp64 sum in row order).
+      for (int c = 0; c < d; ++c) {
+        double sum = 0.0;
+        for (int i = i0; i < i1; ++i) sum += (double)Q[(size_t)i * d + c];
+        qb[c] = (flags & ORC_NO_Q_SMOOTH) ? 0.0f : (float)(sum / (double)(i1 - i0));
+      }
+      // 3. Q codes: one scale per token (a lane owns one query column of S^T on gfx950).
+      for (int i = i0; i < i1; ++i) {
+        float amax = 0.0f;
+        for (int c = 0; c < d; ++c) {
+          qt[c] = Q[(size_t)i * d + c] - qb[c];
+          amax = std::max(amax, std::fabs(qt[c]));
+        }
+        const Int4Scale s = int4_scale(amax);
+        sq[(size_t)h * Lq + i] = s.s;
+        for (int c = 0; c < d; ++c) qcode[((size_t)h * Lq + i) * d + c] = int4_code(qt[c], s.inv);
+      }
+      // 5. Correction term: the block mean's exact contribution q̄·k̃_j, which the smoothed
+      //    INT4 product leaves out. fp64 sum in channel order, scaled to base-2 logit units
+      //    (times sm_scale*log2 e) and rounded once to f32.
+      if (delta) {
+        float* D = delta + ((size_t)h * nqb + b) * Lkv;
+        for (int j = 0; j < Lkv; ++j) {
+          double acc = 0.0;
+          for (int c = 0; c < d; ++c) acc += (double)qb[c] * (double)KT[(size_t)j * d + c];
+          D[j] = (float)(acc * (double)L);
+        }
+      }
+    }
+  });
+  return 0;
+}
+
+// 6. Exact integer QK^T of the codes for rows [row0, row0+nrows): s [Hq][nrows][Lkv].
+int orc_qk_i32(int Hq, int Hkv, int Lq, int Lkv, int d, const int8_t* qcode, const int8_t* kcode,
+               int row0, int nrows, int32_t* s, int nthreads) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || row0 < 0 || nrows < 0 || row0 + nrows > Lq) return -1;
+  parallel_for(Hq, resolve_threads(nthreads), [&](int h) {
+    const int g = h / (Hq / Hkv);
+    for (int r = 0; r < nrows; ++r)
+      for (int j = 0; j < Lkv; ++j) {
+        int32_t acc = 0;
+        for (int c = 0; c < d; ++c)
+          acc += (int32_t)qcode[((size_t)h * Lq + row0 + r) * d + c] *
+                 (int32_t)kcode[((size_t)g * Lkv + j) * d + c];
+        s[((size_t)h * nrows + r) * Lkv + j] = acc;
+      }
+  });
+  return 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+// 7. Dequantized logit of (row i, key j) in base-2 units, in the kernel's f32 precision:
+//    x = S * ((s_q * L) * s_k) + delta'   with one rounding for the product-plus-correction.
+//    Masked entries are -inf. Causal masking is aligned bottom-right: key j is visible from row i
+//    when j <= i + (Lkv - Lq).
+struct LogitCtx {
+  int Hq, Hkv, Lq, Lkv, d, causal;
+  float L;
+  const int8_t *qcode, *kcode;
+  const float *sq, *sk, *delta;
+  int ngk, nqb;
+};
+
+float logit(const LogitCtx& c, int h, int i, int j) {
+  if (c.causal && j > i + (c.Lkv - c.Lq)) return -kInfF;
+  const int g = h / (c.Hq / c.Hkv);
+  int32_t S = 0;
+  for (int ch = 0; ch < c.d; ++ch)
+    S += (int32_t)c.qcode[((size_t)h * c.Lq + i) * c.d + ch] * (int32_t)c.kcode[((size_t)g * c.Lkv + j) * c.d + ch];
+  const float cq = c.sq[(size_t)h * c.Lq + i] * c.L;
+  const float cs = cq * c.sk[(size_t)g * c.ngk + kgroup(j)];
+  const float dl = c.delta ? c.delta[((size_t)h * c.nqb + i / kQBlock) * c.Lkv + j] : 0.0f;
+  return std::fma((float)S, cs, dl);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Logits for rows `rows[0..nrows)` (all rows when rows == NULL): x [Hq][nrows][Lkv] f32.
+int orc_logits(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int causal,
+               const int8_t* qcode, const float* sq, const int8_t* kcode, const float* sk,
+               const float* delta, const int32_t* rows, int nrows, float* x, int nthreads) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lq <= 0 || Lkv <= 0) return -1;
+  if (!rows) nrows = Lq;
+  LogitCtx ctx{Hq, Hkv, Lq, Lkv, d, causal, resolve_scale(sm_scale, d) * kLog2e,
+               qcode, kcode, sq, sk, delta, 2 * ceil_div(Lkv, 32), ceil_div(Lq, kQBlock)};
+  parallel_for(Hq, resolve_threads(nthreads), [&](int h) {
+    for (int r = 0; r < nrows; ++r) {
+      const int i = rows ? rows[r] : r;
+      for (int j = 0; j < Lkv; ++j) x[((size_t)h * nrows + r) * Lkv + j] = logit(ctx, h, i, j);
+    }
+  });
+  return 0;
+}
+
+// 8-9. Online softmax over key tiles of `bn` keys in ascending order, with P~ = e4m3(448*2^(x-m))
+// and the two-level accumulation: each tile's P~V product is formed on its own ("inner") and then
+// folded into the running output O after O is rescaled by alpha = 2^(m_prev - m_new)
+// ([ABS]/[REC] two-level accumulation; [EP] FlashAttention-2 lineage for the online softmax).
+//
+// The row sum l is accumulated from the unquantized p (reading). The factor 448 cancels in O/l.
+// out[i][c] = O[c] * s_v[c] / l, or 0 for a row with no visible key.
+//
+// FP8 decisions: p is 2^t with t = x - (m - log2 448) evaluated in f32 (two f32 roundings, as the
+// kernel does it); the oracle takes 2^t in fp64, while the kernel's hardware exp2 is accurate to
+// about 2^-23.5 relative. A value of p whose e4m3 rounding would change anywhere inside the
+// exponent interval t +- r, r = 2^-20 + 2^-22 (|x| + |m - log2 448|), is "ambiguous": either code is
+// a correct result. For each output element `allow` bounds how far such flips can move it:
+// allow = (sum over ambiguous j of |code step| * |dec(v8[j,c])| * rescale) * s_v[c] / l.
+//
+// q-side inputs are the orc_quantize outputs of the same sequence. out/allow: [Hq][nrows][d] f64.
+int orc_attn_quant(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int causal, int bn,
+                   int flags, const int8_t* qcode, const float* sq, const int8_t* kcode,
+                   const float* sk, const uint8_t* v8, const float* sv, const float* delta,
+                   const int32_t* rows, int nrows, double* out, double* allow, int nthreads) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lq <= 0 || Lkv <= 0 || bn <= 0) return -1;
+  if (!rows) nrows = Lq;
+  LogitCtx ctx{Hq, Hkv, Lq, Lkv, d, causal, resolve_scale(sm_scale, d) * kLog2e,
+               qcode, kcode, sq, sk, delta, 2 * ceil_div(Lkv, 32), ceil_div(Lq, kQBlock)};
+  double vdec[256];
+  for (int c = 0; c < 256; ++c) vdec[c] = e4m3_decode((uint8_t)c);
+  parallel_for(Hq * nrows, resolve_threads(nthreads), [&](int unit) {
+    const int h = unit / nrows, r = unit % nrows;
+    const int i = rows ? rows[r] : r;
+    const int g = h / (Hq / Hkv);
+    std::vector<double> O(d, 0.0), A(d, 0.0), inner(d), ainner(d);
+    std::vector<float> x(bn);
+    float m = -kInfF;
+    double l = 0.0;
+    for (int t0 = 0; t0 < Lkv; t0 += bn) {
+      const int t1 = std::min(Lkv, t0 + bn);
+      float tmax = -kInfF;
+      for (int j = t0; j < t1; ++j) {
+        x[j - t0] = logit(ctx, h, i, j);
+        tmax = std::max(tmax, x[j - t0]);
+      }
+      const float mnew = std::max(m, tmax);
+      if (mnew == -kInfF) continue;  // no visible key yet: nothing to add, nothing to rescale
+      const double alpha = (m == -kInfF) ? 0.0 : std::exp2((double)m - (double)mnew);
+      const float mb = mnew - kLog2_448;
+      std::fill(inner.begin(), inner.end(), 0.0);
+      std::fill(ainner.begin(), ainner.end(), 0.0);
+      double psum = 0.0;
+      for (int j = t0; j < t1; ++j) {
+        const float xj = x[j - t0];
+        if (xj == -kInfF) continue;
+        const float t = xj - mb;
+        const double p = std::exp2((double)t);
+        psum += p;
+        double p8 = p, step = 0.0;
+        if (!(flags & ORC_ATTN_NO_P8)) {
+          const uint8_t code = e4m3_encode(p);
+          p8 = e4m3_decode(code);
+          const double rad = 0x1p-20 + 0x1p-22 * ((double)std::fabs(xj) + (double)std::fabs(mb));
+          const uint8_t lo = e4m3_encode(std::exp2((double)t - rad));
+          const uint8_t hi = e4m3_encode(std::exp2((double)t + rad));
+          if (lo != hi)
+            step = std::max(std::fabs(e4m3_decode(lo) - p8), std::fabs(e4m3_decode(hi) - p8));
+        }
+        const uint8_t* vrow = v8 + ((size_t)g * Lkv + j) * d;
+        for (int c = 0; c < d; ++c) {
+          inner[c] += p8 * vdec[vrow[c]];
+          if (step != 0.0) ainner[c] += step * std::fabs(vdec[vrow[c]]);
+        }
+      }
+      l = alpha * l + psum;
+      for (int c = 0; c < d; ++c) {
+        O[c] = alpha * O[c] + inner[c];
+        A[c] = alpha * A[c] + ainner[c];
+      }
+      m = mnew;
+    }
+    double* o = out + ((size_t)h * nrows + r) * d;
+    double* a = allow ? allow + ((size_t)h * nrows + r) * d : nullptr;
+    for (int c = 0; c < d; ++c) {
+      const double s = sv[(size_t)g * d + c];
+      o[c] = l > 0.0 ? O[c] * s / l : 0.0;
+      if (a) a[c] = l > 0.0 ? A[c] * s / l : 0.0;
+    }
+  });
+  return 0;
+}
+
+// 10. Plain FP64 attention softmax(sm_scale * q k^T) v, two-pass, from the unsmoothed,
+// unquantized inputs: the dense rule the method keeps ([VIZ] page thesis; [ABS]).
+int orc_attn_fp64(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int causal,
+                  const float* q, const float* k, const float* v, const int32_t* rows, int nrows,
+                  double* out, int nthreads) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lq <= 0 || Lkv <= 0) return -1;
+  if (!rows) nrows = Lq;
+  const double tau = (double)resolve_scale(sm_scale, d);
+  parallel_for(Hq * nrows, resolve_threads(nthreads), [&](int unit) {
+    const int h = unit / nrows, r = unit % nrows;
+    const int i = rows ? rows[r] : r;
+    const int g = h / (Hq / Hkv);
+    const float* qi = q + ((size_t)h * Lq + i) * d;
+    std::vector<double> y(Lkv);
+    double ymax = -kInf;
+    for (int j = 0; j < Lkv; ++j) {
+      if (causal && j > i + (Lkv - Lq)) { y[j] = -kInf; continue; }
+      const float* kj = k + ((size_t)g * Lkv + j) * d;
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += (double)qi[c] * (double)kj[c];
+      y[j] = tau * acc;
+      ymax = std::max(ymax, y[j]);
+    }
+    double* o = out + ((size_t)h * nrows + r) * d;
+    std::fill(o, o + d, 0.0);
+    if (ymax == -kInf) return;
+    double wsum = 0.0;
+    for (int j = 0; j < Lkv; ++j) {
+      if (y[j] == -kInf) continue;
+      const double w = std::exp(y[j] - ymax);
+      wsum += w;
+      const float* vj = v + ((size_t)g * Lkv + j) * d;
+      for (int c = 0; c < d; ++c) o[c] += w * (double)vj[c];
+    }
+    for (int c = 0; c < d; ++c) o[c] /= wsum;
+  });
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,503 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself (closed forms,
+invariants, special cases that reduce to a library routine, brute force on tiny inputs).
+
+Which mistake each pin is meant to catch is stated in its docstring.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from quantized_exact_attention_token_amd import workloads as W
+
+LOG2E = np.float32(1.44269504088896340736)
+
+
+def _L(d, sm_scale=0.0):
+    s = np.float32(sm_scale) if sm_scale else np.float32(1.0) / np.sqrt(np.float32(d))
+    return np.float32(s * LOG2E)
+
+
+def _dec_table():
+    return np.array([O.e4m3_decode(c) for c in range(256)])
+
+
+# ------------------------------------------------------------------------------------------------
+# L1: FP8 e4m3 codec
+
+
+def test_e4m3_roundtrip_every_code():
+    """decode->encode is the identity on all 254 finite codes (both zeros included): catches a wrong
+    bias, a wrong subnormal rule or a wrong mantissa width."""
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            assert math.isnan(O.e4m3_decode(c))
+            continue
+        assert O.e4m3_encode(O.e4m3_decode(c)) == c, hex(c)
+    # closed forms from the format: largest finite, smallest normal, smallest subnormal
+    assert O.e4m3_decode(0x7E) == 448.0
+    assert O.e4m3_decode(0x08) == 2.0 ** -6
+    assert O.e4m3_decode(0x01) == 2.0 ** -9
+    assert O.e4m3_decode(0x38) == 1.0
+
+
+def test_e4m3_ties_to_even_and_saturation():
+    """Midpoints between neighbouring codes go to the even mantissa; anything past 448 saturates;
+    values just off a midpoint go to the nearer code."""
+    for c in range(0, 0x7E):
+        lo, hi = O.e4m3_decode(c), O.e4m3_decode(c + 1)
+        mid = (lo + hi) / 2
+        even = c if (c & 1) == 0 else c + 1
+        assert O.e4m3_encode(mid) == even, hex(c)
+        assert O.e4m3_encode(-mid) == 0x80 | even
+        assert O.e4m3_encode(np.nextafter(mid, 0.0)) == c
+        assert O.e4m3_encode(np.nextafter(mid, 1e9)) == c + 1
+    for x in (448.0, 455.9, 464.0, 500.0, 1e30, math.inf):
+        assert O.e4m3_encode(x) == 0x7E
+        assert O.e4m3_encode(-x) == 0xFE
+    assert O.e4m3_encode(-0.0) == 0x80
+    assert O.e4m3_encode(2.0 ** -11) == 0x00      # below half the smallest subnormal
+    assert O.e4m3_encode(2.0 ** -10) == 0x00      # exactly half: tie to even (0)
+    assert O.e4m3_encode(3 * 2.0 ** -10) == 0x02  # 1.5 subnormal steps: tie to even (2)
+
+
+def test_e4m3_matches_torch_cast_in_range():
+    """Cross-check against torch's float32 -> float8_e4m3fn cast (a library routine) on in-range
+    values, including exact midpoints."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        np.exp2(rng.uniform(-12, 8.8, 20000)) * rng.choice([-1, 1], 20000),
+        [(O.e4m3_decode(c) + O.e4m3_decode(c + 1)) / 2 for c in range(0x7E)],
+    ]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = np.array([O.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------------------------------------------------
+# helpers
+
+
+def _seq(w, b=0):
+    """One sequence of a workload as head-major float32 arrays (exact widening)."""
+    q, k, v, cu = W.generate(w)
+    if cu is not None:
+        s, e = int(cu[b]), int(cu[b + 1])
+        q, k, v = q[s:e], k[s:e], v[s:e]
+    else:
+        q, k, v = q[b], k[b], v[b]
+    f = lambda t: t.float().permute(1, 0, 2).contiguous().numpy()
+    return f(q), f(k), f(v)
+
+
+def _cos(a, b):
+    a, b = a.ravel().astype(np.float64), b.ravel().astype(np.float64)
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+# ------------------------------------------------------------------------------------------------
+# smoothing statistics
+
+
+def test_means_match_exact_sums():
+    """k̄ and q̄ equal the exactly-summed means (fp16 inputs of moderate size sum exactly in fp64,
+    so numpy's fp64 mean is the same closed form): catches a wrong axis, a wrong count for a ragged
+    last Q block, or a mean over the wrong tokens."""
+    w = W.custom(1, 4, 2, 300, 333, 64, torch.float16, seed=3, q_offset_std=2.0)
+    q, k, v = _seq(w)
+    z = O.quantize(q, k, v)
+    kbar = (k.astype(np.float64).sum(axis=1) / k.shape[1]).astype(np.float32)
+    assert np.array_equal(z.kbar, kbar)
+    for b in range(z.qbar.shape[1]):
+        rows = q[:, 128 * b:min(q.shape[1], 128 * b + 128)].astype(np.float64)
+        qb = (rows.sum(axis=1) / rows.shape[1]).astype(np.float32)
+        assert np.array_equal(z.qbar[:, b], qb), b
+
+
+def test_k_shift_invariance_quantized():
+    """I1: adding a constant vector c to every key changes k̄ by exactly c and nothing else in the
+    quantized pipeline (inputs on a grid where every sum is exact): catches a dropped or misplaced
+    K mean subtraction."""
+    rng = np.random.default_rng(11)
+    Hq, Hkv, L, d = 2, 1, 64, 64
+    q = (rng.integers(-64, 64, (Hq, L, d)) / 16).astype(np.float32)
+    k = (rng.integers(-64, 64, (Hkv, L, d)) / 16).astype(np.float32)
+    v = rng.standard_normal((Hkv, L, d)).astype(np.float32)
+    c = rng.integers(-50, 50, (1, 1, d)).astype(np.float32)
+    z0, z1 = O.quantize(q, k, v), O.quantize(q, k + c, v)
+    assert np.array_equal(z1.kbar, z0.kbar + c[0])
+    for name in ("kcode", "sk", "qcode", "sq", "delta"):
+        assert np.array_equal(getattr(z0, name), getattr(z1, name)), name
+    o0, _ = O.attn_quant(z0, False)
+    o1, _ = O.attn_quant(z1, False)
+    assert np.array_equal(o0, o1)
+    # without the K mean subtraction the codes do change
+    zn = O.quantize(q, k + c, v, flags=O.NO_K_SMOOTH)
+    assert not np.array_equal(zn.kcode, z0.kcode)
+
+
+def test_k_shift_invariance_fp64():
+    """I1 for the exact reference: softmax ignores a per-row constant, so shifting every key by c
+    leaves FP64 attention unchanged (to rounding)."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((2, 40, 64)).astype(np.float32)
+    k = (np.round(rng.standard_normal((2, 50, 64)) * 1024) / 1024).astype(np.float32)  # k + c exact
+    v = rng.standard_normal((2, 50, 64)).astype(np.float32)
+    c = (rng.integers(-8, 8, (1, 1, 64))).astype(np.float32)
+    a = O.attn_fp64(q, k, v, False)
+    b = O.attn_fp64(q, k + c, v, False)
+    assert np.max(np.abs(a - b)) < 1e-12 * 50
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Lq,Lkv", [(37, 37), (20, 45), (45, 20)])
+def test_fp64_matches_torch_sdpa(causal, Lq, Lkv):
+    """The exact reference equals torch's scaled-dot-product attention in float64 (a library
+    routine), with a bottom-right aligned causal mask; GQA by repeating K/V heads."""
+    rng = np.random.default_rng(13)
+    Hq, Hkv, d = 4, 2, 64
+    q = rng.standard_normal((Hq, Lq, d)).astype(np.float32)
+    k = rng.standard_normal((Hkv, Lkv, d)).astype(np.float32)
+    v = rng.standard_normal((Hkv, Lkv, d)).astype(np.float32)
+    ours = O.attn_fp64(q, k, v, causal)
+    tq = torch.from_numpy(q).double()
+    tk = torch.from_numpy(k).double().repeat_interleave(Hq // Hkv, 0)
+    tv = torch.from_numpy(v).double().repeat_interleave(Hq // Hkv, 0)
+    mask = None
+    if causal:
+        i = torch.arange(Lq)[:, None]
+        j = torch.arange(Lkv)[None, :]
+        mask = j <= i + (Lkv - Lq)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    ref = ref.numpy()
+    if causal and Lq > Lkv:  # rows with no visible key: the method outputs 0
+        dead = np.arange(Lq) + (Lkv - Lq) < 0
+        ref[:, dead] = 0.0
+    assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+# ------------------------------------------------------------------------------------------------
+# INT4 quantizer
+
+
+def test_int4_round_trip_bound():
+    """I3: every smoothed value is within half a step of its reconstruction, every code is in
+    [-7, 7] and each nonzero group reaches +-7 at its largest element: catches a wrong scale, a
+    wrong rounding, or a code computed against another group's scale."""
+    w = W.custom(1, 4, 2, 200, 230, 128, torch.bfloat16, seed=5, n_outliers=3, outlier_scale=20.0,
+                 k_offset_std=4.0)
+    q, k, v = _seq(w)
+    z = O.quantize(q, k, v)
+    qt = q - np.repeat(z.qbar, 128, axis=1)[:, :q.shape[1]]
+    rec = z.sq[..., None] * z.qcode
+    assert np.all(np.abs(qt - rec) <= z.sq[..., None] / 2 * (1 + 2 ** -20))
+    assert np.all(np.abs(z.qcode) <= 7)
+    assert np.all(np.abs(z.qcode).max(axis=2)[z.sq > 0] == 7)
+    kt = k - z.kbar[:, None, :]
+    grp = np.array([O.kgroup(j) for j in range(k.shape[1])])
+    skj = z.sk[:, grp]
+    assert np.all(np.abs(kt - skj[..., None] * z.kcode) <= skj[..., None] / 2 * (1 + 2 ** -20))
+    for g in range(z.sk.shape[1]):
+        members = grp == g
+        if members.any():
+            assert np.abs(z.kcode[:, members]).max() == 7
+
+
+def test_k_groups_follow_lane_halves():
+    """The K scale groups are the two 16-key halves of each 32-key tile split on bit 2 of the key
+    index (the keys one gfx950 MFMA lane half owns). Scaling exactly those keys by 1000 scales
+    exactly the odd groups' scales: a contiguous or strided grouping fails."""
+    rng = np.random.default_rng(21)
+    L, d = 96, 64
+    k = rng.standard_normal((1, L, d)).astype(np.float32)
+    sel = ((np.arange(L) >> 2) & 1) == 1
+    k2 = k.copy()
+    k2[:, sel] *= 1000
+    q = rng.standard_normal((1, 8, d)).astype(np.float32)
+    # the K mean is switched off here: it is not under test and the scaled keys would dominate it
+    z = O.quantize(q, k2, k2, flags=O.NO_K_SMOOTH)
+    ratio = z.sk[0, 1::2] / z.sk[0, 0::2]
+    assert np.all(ratio > 300), ratio
+    assert [O.kgroup(j) for j in range(32)] == [((j >> 2) & 1) for j in range(32)]
+
+
+# ------------------------------------------------------------------------------------------------
+# correction term and logits
+
+
+def _grid_inputs(rng, Hq, Lq, Lkv, d, qbar_val):
+    """Q rows in +-pairs around a chosen block mean, K rows in +-pairs around a per-channel offset:
+    every mean is exact, every smoothed value an integer in [-7, 7] with a 7 in each row/group."""
+    assert Lq % 2 == 0 and Lkv % 32 == 0
+    qt = rng.integers(-7, 8, (Hq, Lq // 2, d)).astype(np.float32)
+    qt[:, :, 0] = 7
+    qt = np.stack([qt, -qt], axis=2).reshape(Hq, Lq, d)
+    kt = rng.integers(-7, 8, (1, Lkv // 2, d)).astype(np.float32)
+    kt[:, :, 1] = 7
+    kt = np.stack([kt, -kt], axis=2).reshape(1, Lkv, d)
+    koff = rng.integers(-20, 20, (1, 1, d)).astype(np.float32)
+    return qt + qbar_val, kt + koff, qt, kt
+
+
+def test_lossless_grid_codes_and_integer_product():
+    """Z2: smoothed values that already lie on the INT4 grid quantize losslessly (scale 1, codes
+    equal values) and the integer product equals numpy's exact integer matmul: catches a transposed
+    operand or a wrong index in S."""
+    rng = np.random.default_rng(31)
+    Hq, Lq, Lkv, d = 2, 128, 64, 64
+    qbar = (rng.integers(-16, 16, (Hq, 1, d)) / 8).astype(np.float32)
+    q, k, qt, kt = _grid_inputs(rng, Hq, Lq, Lkv, d, qbar)
+    v = rng.standard_normal((1, Lkv, d)).astype(np.float32)
+    z = O.quantize(q, k, v)
+    assert np.all(z.sq == 1.0) and np.all(z.sk == 1.0)
+    assert np.array_equal(z.qcode, qt.astype(np.int8))
+    assert np.array_equal(z.kcode, kt.astype(np.int8))
+    S = O.qk_i32(z)
+    ref = np.einsum("hid,jd->hij", qt.astype(np.int64), kt[0].astype(np.int64))
+    assert np.array_equal(S, ref)
+
+
+def test_q_correction_restores_logits():
+    """I2: with lossless INT4 codes, the dequantized logits plus the correction q̄·k̃ equal the exact
+    smoothed-K logits L·q·k̃, and differ from the unsmoothed L·q·k by a per-row constant L·q·k̄ that
+    softmax ignores: catches a dropped correction term or a wrong sign."""
+    rng = np.random.default_rng(32)
+    Hq, Lq, Lkv, d = 2, 256, 96, 64
+    qbar = (rng.integers(-24, 24, (Hq, 1, d)) / 8).astype(np.float32)
+    q, k, qt, kt = _grid_inputs(rng, Hq, Lq, Lkv, d, qbar)
+    v = rng.standard_normal((1, Lkv, d)).astype(np.float32)
+    z = O.quantize(q, k, v)
+    x = O.logits(z, False).astype(np.float64)
+    L = float(_L(d))
+    exact = L * np.einsum("hid,jd->hij", q.astype(np.float64), kt[0].astype(np.float64))
+    assert np.max(np.abs(x - exact) / (np.abs(exact) + 1)) < 2 ** -20
+    raw = L * np.einsum("hid,jd->hij", q.astype(np.float64), k[0].astype(np.float64))
+    diff = x - raw
+    assert np.max(np.abs(diff - diff[:, :, :1])) < 1e-3 * (1 + np.abs(raw).max())
+    # the ablation without Q smoothing has no correction and a different grid: logits still close
+    # to exact only up to quantization error; dropping the correction on its own would be far off
+    x_no = x - np.repeat(z.delta, 128, axis=1)[:, :Lq].astype(np.float64)
+    assert np.max(np.abs(x_no - exact)) > 1.0
+
+
+def test_delta_is_mean_times_smoothed_k():
+    """The stored correction equals L·(q̄·k̃) computed with numpy's fp64 matmul (library routine),
+    within the single f32 rounding."""
+    w = W.custom(1, 4, 2, 300, 200, 64, torch.float16, seed=9, q_offset_std=2.0)
+    q, k, v = _seq(w)
+    z = O.quantize(q, k, v)
+    kt = (k - z.kbar[:, None, :]).astype(np.float64)
+    ref = np.einsum("hbd,hjd->hbj", z.qbar.astype(np.float64), np.repeat(kt, 2, axis=0))
+    ref *= float(_L(64))
+    assert np.max(np.abs(z.delta - ref) / (np.abs(ref) + 1e-30)) <= 2 ** -23
+
+
+def test_logits_within_int4_error_bound():
+    """The dequantized logits differ from the exact smoothed logits L·q·(k - k̄) by no more than
+    the closed-form INT4 bound L·sum_c(|q̃| s_k/2 + |k̃| s_q/2 + s_q s_k/4) (plus f32 slack):
+    catches a scale taken from the wrong token or group."""
+    w = W.custom(1, 2, 1, 256, 200, 128, torch.bfloat16, seed=10, n_outliers=3, outlier_scale=20.0,
+                 k_offset_std=4.0, q_offset_std=1.0)
+    q, k, v = _seq(w)
+    z = O.quantize(q, k, v)
+    x = O.logits(z, False).astype(np.float64)
+    L = float(_L(128))
+    qt = (q - np.repeat(z.qbar, 128, axis=1)[:, :q.shape[1]]).astype(np.float64)
+    kt = (k - z.kbar[:, None, :]).astype(np.float64)
+    kt2 = np.repeat(kt, 2, axis=0)
+    exact = L * np.einsum("hid,hjd->hij", q.astype(np.float64), kt2)
+    grp = np.array([O.kgroup(j) for j in range(k.shape[1])])
+    skj = np.repeat(z.sk[:, grp], 2, axis=0).astype(np.float64)    # [Hq, Lkv]
+    sq = z.sq.astype(np.float64)                                    # [Hq, Lq]
+    bound = L * (np.abs(qt).sum(-1)[:, :, None] * skj[:, None, :] / 2
+                 + np.abs(kt2).sum(-1)[:, None, :] * sq[:, :, None] / 2
+                 + 128 * sq[:, :, None] * skj[:, None, :] / 4)
+    err = np.abs(x - exact)
+    assert np.all(err <= bound * (1 + 1e-5) + 1e-4 * (1 + np.abs(exact)))
+    assert err.max() > 0  # not vacuous
+
+
+# ------------------------------------------------------------------------------------------------
+# online softmax and two-level accumulation
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_equals_two_pass(causal):
+    """I4: with P~ left unquantized, the tiled online softmax with the rescale-and-fold equals a
+    two-pass softmax over the same logits for any tile size: catches a wrong rescale factor, a
+    missing fold or a max that is not carried across tiles."""
+    w = W.custom(1, 2, 1, 150, 150, 64, torch.float16, seed=14)
+    q, k, v = _seq(w)
+    z = O.quantize(q, k, v)
+    x = O.logits(z, causal).astype(np.float64)
+    dec = _dec_table()
+    V = dec[z.v8[0]] * z.sv[0][None, :]
+    M = x.max(axis=2, keepdims=True)
+    wgt = np.exp2(x - M)
+    ref = np.einsum("hij,jc->hic", wgt, V) / wgt.sum(axis=2, keepdims=True)
+    for bn in (1, 16, 64, 150):
+        out, _ = O.attn_quant(z, causal, bn=bn, flags=O.ATTN_NO_P8)
+        assert np.max(np.abs(out - ref)) < 1e-5 * np.abs(V).max(), bn
+
+
+def test_p8_rounding_effect_bounded():
+    """B1: quantizing P~ to e4m3 changes each weight by at most 2^-4 relative (3 mantissa bits),
+    so the output moves by at most 2^-4·max|v| against the unquantized form."""
+    wl = W.WORKLOADS["tiny"]
+    q, k, v = _seq(wl)
+    z = O.quantize(q, k, v)
+    a, _ = O.attn_quant(z, False)
+    b, _ = O.attn_quant(z, False, flags=O.ATTN_NO_P8)
+    vmax = (_dec_table()[z.v8] * z.sv[:, None, :]).max()
+    diff = np.abs(a - b).max()
+    assert 0 < diff <= 2 ** -4 * vmax
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_value_mean(causal):
+    """Z1: Q = 0 makes every logit 0, so every P~ is exactly 448 and the output is the plain mean of
+    the decoded values (the prefix mean under a causal mask)."""
+    rng = np.random.default_rng(41)
+    L, d = 100, 64
+    q = np.zeros((2, L, d), np.float32)
+    k = rng.standard_normal((1, L, d)).astype(np.float32)
+    v = rng.standard_normal((1, L, d)).astype(np.float32)
+    z = O.quantize(q, k, v)
+    out, allow = O.attn_quant(z, causal)
+    V = _dec_table()[z.v8[0]] * z.sv[0][None, :]
+    if causal:
+        ref = np.cumsum(V, axis=0) / np.arange(1, L + 1)[:, None]
+    else:
+        ref = np.broadcast_to(V.mean(axis=0), (L, d))
+    assert np.max(np.abs(out - ref[None])) < 1e-6 * np.abs(V).max()
+    assert np.all(allow == 0)
+
+
+def test_single_key_returns_its_value():
+    """Z3: with one key the output is that key's value up to the FP8 step of V."""
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((2, 5, 64)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    z = O.quantize(q, k, v)
+    out, _ = O.attn_quant(z, False)
+    ref = _dec_table()[z.v8[0, 0]] * z.sv[0]
+    assert np.max(np.abs(out - ref)) < 1e-6
+    assert np.max(np.abs(out - v[0, 0])) <= np.abs(v).max() * 2 ** -4
+
+
+def test_one_hot_attention():
+    """Z4: a logit gap far beyond the FP8 range makes every other P~ zero: the output is the
+    winning key's value."""
+    rng = np.random.default_rng(43)
+    L, d = 130, 64
+    q = np.zeros((1, 4, d), np.float32)
+    q[:, :, 0] = 30.0
+    q[:, 1::2, 0] = 20.0
+    k = (rng.standard_normal((1, L, d)) * 0.1).astype(np.float32)
+    k[0, 77, 0] = 60.0
+    v = rng.standard_normal((1, L, d)).astype(np.float32)
+    z = O.quantize(q, k, v)
+    out, _ = O.attn_quant(z, False)
+    ref = _dec_table()[z.v8[0, 77]] * z.sv[0]
+    # the winner's own weight is 448 in P~ but 2^t with t = x - (x - log2 448) in f32 in the row
+    # sum: a relative difference of at most two f32 roundings at the logit's magnitude
+    xmax = float(np.abs(O.logits(z, False)).max())
+    tol = 2.0 ** -22 * (xmax + 16) * np.abs(ref).max()
+    assert np.max(np.abs(out - ref)) <= tol
+
+
+def test_gqa_equals_repeated_kv():
+    """E1: grouped-query attention equals multi-head attention with each kv head repeated for its
+    consecutive q heads, bit for bit: catches a wrong q-head -> kv-head map."""
+    w = W.custom(1, 4, 2, 140, 170, 64, torch.float16, seed=15)
+    q, k, v = _seq(w)
+    z1 = O.quantize(q, k, v)
+    z2 = O.quantize(q, np.repeat(k, 2, axis=0), np.repeat(v, 2, axis=0))
+    for causal in (False, True):
+        a, _ = O.attn_quant(z1, causal)
+        b, _ = O.attn_quant(z2, causal)
+        assert np.array_equal(a, b)
+
+
+def test_fully_masked_rows_are_zero():
+    """With Lq > Lkv and a bottom-right causal mask the first Lq - Lkv rows see no key and output 0."""
+    rng = np.random.default_rng(44)
+    q = rng.standard_normal((1, 80, 64)).astype(np.float32)
+    k = rng.standard_normal((1, 50, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 50, 64)).astype(np.float32)
+    z = O.quantize(q, k, v)
+    out, _ = O.attn_quant(z, True)
+    assert np.all(out[:, :30] == 0) and np.all(np.abs(out[:, 30:]).sum(-1) > 0)
+
+
+# ------------------------------------------------------------------------------------------------
+# whole method vs the exact rule
+
+
+def test_quantized_pipeline_vs_exact_on_outliers():
+    """Q1 on the tiny outlier workload: smoothing beats the naive pipeline (the pages show naive
+    INT4 shifting softmax winners), and an independent numpy quantize-dequantize simulation of the
+    same groups (fp64, library softmax) lands at the same accuracy. The outliers here are zero-mean
+    channel multipliers, which a mean subtraction cannot remove, so INT4 keeps only about cos 0.93
+    against the exact result; a value far from the simulation signals a mistake in the oracle."""
+    wl = W.WORKLOADS["tiny"]
+    q, k, v = _seq(wl)
+    exact = O.attn_fp64(q, k, v, wl.causal)
+    z = O.quantize(q, k, v)
+    out, _ = O.attn_quant(z, wl.causal)
+    zn = O.quantize(q, k, v, flags=O.NO_K_SMOOTH | O.NO_Q_SMOOTH)
+    naive, _ = O.attn_quant(zn, wl.causal)
+    c_s, c_n = _cos(out, exact), _cos(naive, exact)
+    assert c_n < c_s, (c_n, c_s)
+    # independent simulation: dequantized Q (block mean + per-token INT4) and K (per 16-key group)
+    Q, K, V = (a.astype(np.float64) for a in (q, k, v))
+    kt = K - K.mean(axis=1, keepdims=True)
+    nb = (Q.shape[1] + 127) // 128
+    qb = np.concatenate([np.repeat(Q[:, 128 * b:128 * b + 128].mean(1, keepdims=True),
+                                   min(128, Q.shape[1] - 128 * b), 1) for b in range(nb)], 1)
+    qt = Q - qb
+    sq = np.abs(qt).max(-1, keepdims=True) / 7
+    qd = np.round(qt / sq) * sq + qb
+    grp = 2 * (np.arange(K.shape[1]) // 32) + ((np.arange(K.shape[1]) >> 2) & 1)
+    kd = np.zeros_like(kt)
+    for g in np.unique(grp):
+        m = grp == g
+        s = np.abs(kt[:, m]).max(axis=(1, 2), keepdims=True) / 7
+        kd[:, m] = np.round(kt[:, m] / s) * s
+    t = torch.from_numpy
+    sim = torch.nn.functional.scaled_dot_product_attention(t(qd), t(kd), t(V)).numpy()
+    c_sim = _cos(sim, exact)
+    assert abs(c_s - c_sim) < 0.02, (c_s, c_sim)
+    assert 0.85 < c_s < 0.99, c_s
+
+
+def test_quantized_pipeline_close_to_exact_without_outliers():
+    """Without channel multipliers (offsets only, which smoothing removes exactly) the pipeline
+    reaches cos >= 0.99 against FP64 attention; dropping the Q correction term breaks it."""
+    w = W.custom(1, 2, 2, 384, 384, 64, torch.float16, seed=17, n_outliers=0, k_offset_std=4.0,
+                 q_offset_std=4.0)
+    q, k, v = _seq(w)
+    exact = O.attn_fp64(q, k, v, False)
+    z = O.quantize(q, k, v)
+    out, _ = O.attn_quant(z, False)
+    assert _cos(out, exact) >= 0.99, _cos(out, exact)
+    z.delta[:] = 0.0
+    broken, _ = O.attn_quant(z, False)
+    assert _cos(broken, exact) < 0.9
+
+
+def test_q_smoothing_matters_with_q_offset():
+    """With a large per-channel Q mean the Q smoothing plus correction improves accuracy over
+    K smoothing alone."""
+    w = W.custom(1, 2, 2, 256, 256, 64, torch.float16, seed=16, q_offset_std=4.0,
+                 k_offset_rademacher=4.0, n_outliers=0, k_offset_std=0.0)
+    q, k, v = _seq(w)
+    exact = O.attn_fp64(q, k, v, False)
+    full, _ = O.attn_quant(O.quantize(q, k, v), False)
+    konly, _ = O.attn_quant(O.quantize(q, k, v, flags=O.NO_Q_SMOOTH), False)
+    assert np.abs(full - exact).max() < np.abs(konly - exact).max()
+    assert _cos(full, exact) > 0.99
