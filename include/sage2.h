@@ -1,0 +1,142 @@
+/* sage2.h — C ABI of the MI355X (gfx950) SageAttention2 forward pass.
+ *
+ * What is computed (PMLR vol. 267 page "SageAttention2: Efficient Attention with Thorough Outlier
+ * Smoothing and Per-thread INT4 Quantization", Abstract; research record of the same title,
+ * "Three components"): dense softmax attention O = softmax(sm_scale * Q K^T) V, evaluated with
+ *   - K smoothing: K minus its per-channel token mean (visual companion "SageAttention2 and Fast
+ *     Exact INT4 Attention", section "Channel Outlier Smoothing");
+ *   - Q smoothing: Q minus the mean of each 128-token block, with the block mean's exact
+ *     contribution (mean . smoothed key) added back into the logits;
+ *   - INT4 Q and K at thread granularity: one scale per query token and one per 16-key group, the
+ *     keys that one half of a 64-lane wave owns in a 32x32 MFMA output tile (section "Per-Thread
+ *     INT4 Geometry" gives thread-owned scale groups; this is their gfx950 form);
+ *   - INT32-exact QK^T, dequantization and an online softmax;
+ *   - P~ and V in FP8 (OCP e4m3), P~V on FP8 MFMA with a two-level accumulation: each short MFMA
+ *     run is folded into an FP32 buffer (section "Numerical Repair Stack": periodic FP32 foldback).
+ * The interface envelope (variable lengths, grouped-query heads, q/kv lengths that differ, head dim
+ * 64 or 128 only, larger rejected) follows section "Implementation envelope" of the visual companion.
+ *
+ * Two calls do the work: sage2_quantize_smooth (the pre-pass: smoothing statistics, INT4/FP8 codes,
+ * scales, correction table, written into a caller-provided workspace) and sage2_attn_fwd (the
+ * attention kernel, reading only the workspace). A workspace may serve any number of attn_fwd calls
+ * made with the same parameters.
+ *
+ * Conventions for every call:
+ *   - Pointers named "device" are HIP device addresses; "host" pointers are CPU memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). All device work is
+ *     enqueued on it; no call synchronizes, allocates or frees memory, or keeps a pointer after it
+ *     returns. There are no host callbacks, so calls may be captured in a HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued; on an error nothing is
+ *     enqueued. A failed launch returns SAGE2_ERR_HIP. Faults during execution surface at the
+ *     caller's next synchronization.
+ *   - NaN or Inf inputs give unspecified outputs (but no out-of-bounds access).
+ *   - The library has no mutable global state and may be called from several threads.
+ */
+#ifndef SAGE2_H
+#define SAGE2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE2_OK = 0,
+  SAGE2_ERR_NULL = 1,         /* a required pointer is NULL */
+  SAGE2_ERR_SHAPE = 2,        /* bad sizes: B/H/N <= 0, H_q % H_kv != 0, bad cu_seqlens, ... */
+  SAGE2_ERR_UNSUPPORTED = 3,  /* head dim not 64/128, unknown dtype, non-finite sm_scale, ... */
+  SAGE2_ERR_ALIGN = 4,        /* pointer or stride not 16-byte aligned; workspace not 256-byte aligned */
+  SAGE2_ERR_WORKSPACE = 5,    /* ws_bytes smaller than sage2_workspace_size() */
+  SAGE2_ERR_HIP = 6           /* a kernel launch failed */
+} sage2_status;
+
+typedef enum { SAGE2_F16 = 0, SAGE2_BF16 = 1, SAGE2_F32 = 2 } sage2_dtype;
+
+typedef struct {
+  /* Sizes. Dense batch: B sequences of N_q queries and N_kv keys each.
+   * Variable length (cu_seqlens set): B sequences packed along the token axis; N_q / N_kv are upper
+   * bounds on the per-sequence lengths (used only to size the launch grids). */
+  int32_t B, H_q, H_kv, N_q, N_kv, d;
+  /* 0 or 1. Causal masks are aligned bottom-right: key j is visible from query i when
+   * j <= i + (L_kv - L_q) within a sequence; a row that sees no key outputs zeros. */
+  int32_t causal;
+  int32_t in_dtype;   /* sage2_dtype of q, k, v: SAGE2_F16 or SAGE2_BF16 */
+  int32_t out_dtype;  /* sage2_dtype of o: SAGE2_F16, SAGE2_BF16 or SAGE2_F32 */
+  float sm_scale;     /* softmax scale; 0 selects 1/sqrt(d) */
+  /* Variable-length batches: cumulative token offsets, B+1 entries, first 0, non-decreasing.
+   * Set all four or none. The device copies are read by the kernels, the host copies size the
+   * workspace and are validated; both must hold the same values. Sequences may be empty. */
+  const int32_t* cu_seqlens_q;        /* device */
+  const int32_t* cu_seqlens_kv;       /* device */
+  const int32_t* cu_seqlens_q_host;   /* host */
+  const int32_t* cu_seqlens_kv_host;  /* host */
+  /* Element strides of q, k, v, o: [0] batch, [1] token, [2] head; the channel stride is 1.
+   * Dense [B, N, H, d] and [B, H, N, d] layouts are both expressed this way. In variable-length
+   * mode the tensors are packed [total_tokens, H, d] and the batch stride is ignored.
+   * Strides times the element size must be multiples of 16 bytes. */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+} sage2_params;
+
+/* Byte offsets (from the workspace base) and byte sizes of the workspace buffers, for tests that
+ * decode the pre-pass outputs. Row counts are padded per sequence: Q rows to a multiple of 128,
+ * K/V rows to a multiple of 128. Layouts (head-major; "row" = padded token slot):
+ *   seq_table  int32 [B][8]: q_start, q_len, kv_start, kv_len, q_row0, kv_row0, qblk0, delta0
+ *   k_partial  f64   [H_kv][kv_rows/128][d]   per-128-token fp64 sums of K
+ *   v_partial  f32   [H_kv][kv_rows/128][d]   per-128-token max |V|
+ *   kbar       f32   [B][H_kv][d]             K channel means
+ *   sv, sv_inv f32   [B][H_kv][d]             V channel scale amax/448 and its inverse 448/amax
+ *   qbar       f32   [H_q][q_blocks][d]       Q block means
+ *   qcode      u8    [H_q][q_rows][d/2]       INT4 codes, channel 2i in the low nibble of byte i
+ *   sq         f32   [H_q][q_rows]            per-token Q scale
+ *   kcode      u8    [H_kv][kv_rows][d/2]     INT4 codes, same nibble order
+ *   sk         f32   [H_kv][kv_rows/16]       K scale of group 2*(j/32) + bit 2 of j
+ *   v8         u8    [H_kv][kv_rows/64][d][2][32]  FP8 e4m3 codes of V*sv_inv; within a 64-key
+ *                                             tile, channel c, half h, slot s holds key
+ *                                             32*(s/16) + 8*((s%16)/4) + 4*h + s%4
+ *   delta      f32   [H_q][delta_len]         correction (qbar . smoothed k_j) * sm_scale * log2(e),
+ *                                             per sequence a [q_blocks][kv_rows] block at delta0
+ */
+typedef struct {
+  int64_t total_bytes;
+  int64_t q_rows, kv_rows, q_blocks, delta_len;  /* per head, summed over sequences */
+  int64_t seq_table, k_partial, v_partial, kbar, sv, sv_inv, qbar, qcode, sq, kcode, sk, v8, delta;
+} sage2_ws_layout;
+
+/* Workspace bytes needed for `p` (validates p first). `bytes` is host memory. */
+sage2_status sage2_workspace_size(const sage2_params* p, size_t* bytes);
+
+/* Pre-pass: smoothing statistics, INT4 codes and scales for Q and K, FP8 codes and scales for V,
+ * and the correction table (abstract: Q,K to INT4, P~,V to FP8, smoothed Q; research record:
+ * component 1 and 2). q, k, v: device, in_dtype, layout per the strides. ws: device, 256-byte
+ * aligned, ws_bytes >= sage2_workspace_size(p). Overwrites the whole workspace region in use. */
+sage2_status sage2_quantize_smooth(const sage2_params* p, const void* q, const void* k,
+                                   const void* v, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention: INT4 QK^T (exact INT32), dequantization with the per-token and per-group scales plus
+ * the correction term, online softmax, FP8 P~V with the two-level FP32 fold, division by the row
+ * sum and the V channel scale. ws: a workspace filled by sage2_quantize_smooth with the same p
+ * (read only). o: device, out_dtype, layout per o_stride; every valid (token, head) row is written. */
+sage2_status sage2_attn_fwd(const sage2_params* p, const void* ws, size_t ws_bytes, void* o,
+                            void* stream);
+
+/* Static English text for a status code. */
+const char* sage2_status_string(sage2_status s);
+
+/* ---- test-only exports ------------------------------------------------------------------------ */
+
+/* Workspace layout of p (host struct). */
+sage2_status sage2_workspace_layout(const sage2_params* p, sage2_ws_layout* out);
+
+/* Exact INT32 Q K^T of the INT4 codes, computed by the attention kernel's own MFMA path, for query
+ * rows [q_begin, q_begin + q_count) of every sequence and q head: s_out (device) int32
+ * [B][H_q][q_count][N_kv]; entries past a sequence's lengths are written as 0. */
+sage2_status sage2_debug_qk_i32(const sage2_params* p, const void* ws, size_t ws_bytes,
+                                int32_t q_begin, int32_t q_count, int32_t* s_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE2_H */

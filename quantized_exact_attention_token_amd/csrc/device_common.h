@@ -1,0 +1,67 @@
+// Device helpers shared by the pre-pass and attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sage2_internal.h"
+
+namespace sage2 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct Seq {
+  int32_t q_start, q_len, kv_start, kv_len, q_row0, kv_row0, qblk0, delta0;
+};
+
+__device__ inline Seq load_seq(const KArgs& a, int b) {
+  const int32_t* t = reinterpret_cast<const int32_t*>(a.ws + a.lay.seq_table) + b * kSeqCols;
+  Seq s;
+  s.q_start = t[kQStart]; s.q_len = t[kQLen]; s.kv_start = t[kKVStart]; s.kv_len = t[kKVLen];
+  s.q_row0 = t[kQRow0]; s.kv_row0 = t[kKVRow0]; s.qblk0 = t[kQBlk0]; s.delta0 = t[kDelta0];
+  return s;
+}
+
+template <typename T>
+__device__ inline T* ws_ptr(const KArgs& a, int64_t off) {
+  return reinterpret_cast<T*>(a.ws + off);
+}
+
+// Exact widening of one fp16 / bf16 element (IN = sage2_dtype).
+template <int IN>
+__device__ inline float ld_in(const void* base, int64_t idx) {
+  const uint16_t raw = reinterpret_cast<const uint16_t*>(base)[idx];
+  if constexpr (IN == SAGE2_BF16) {
+    return __uint_as_float((uint32_t)raw << 16);
+  } else {
+    _Float16 h;
+    __builtin_memcpy(&h, &raw, 2);
+    return (float)h;
+  }
+}
+
+// Element index of (token, head, channel 0) of sequence b in a strided input.
+__device__ inline int64_t row_index(const int64_t* s, int b, int64_t token, int head) {
+  return (int64_t)b * s[0] + token * s[1] + (int64_t)head * s[2];
+}
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Two f32 -> two OCP e4m3 bytes (round to nearest even), into bytes 0-1 (hi = false) or 2-3
+// (hi = true) of `old`.
+__device__ inline int cvt_fp8x2(float a, float b, int old, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true)
+            : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+}
+
+}  // namespace sage2

@@ -1,0 +1,315 @@
+// Pre-pass of the SageAttention2 forward pass on gfx950: smoothing statistics, INT4 codes and
+// scales for Q and K, FP8 codes and scales for V, and the Q-smoothing correction table.
+//
+// Sources: PMLR vol. 267 page "SageAttention2: Efficient Attention with Thorough Outlier Smoothing
+// and Per-thread INT4 Quantization", Abstract (Q,K to INT4 at thread granularity, P~,V to FP8, Q
+// smoothing); research record of the same title, "Three components" (Q smoothing; per-thread scales);
+// visual companion "SageAttention2 and Fast Exact INT4 Attention", "Channel Outlier Smoothing"
+// (K smoothing) and "Per-Thread INT4 Geometry" (scale groups follow thread ownership).
+//
+// Every step that produces a code or a statistic uses a fixed order of IEEE operations (fp64 sums
+// in token order over 128-token chunks, then chunks in order; f32 products and divisions, round to
+// nearest even), so its result is reproducible bit for bit. Built with -ffp-contract=off.
+//
+// The pre-pass streams Q, K and V (HBM-bound); the correction table is a small fp64 product.
+#include "device_common.h"
+
+namespace sage2 {
+namespace {
+
+// ---- plan: per-sequence offsets into the padded workspace buffers ------------------------------
+// One thread walks the sequences in order. A sequence whose device lengths disagree with what the
+// host sized the workspace for (lengths above N, or totals past the layout) gets length 0, so no
+// kernel touches memory outside the workspace.
+__global__ void k_plan(KArgs a) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int32_t* t = ws_ptr<int32_t>(a, a.lay.seq_table);
+  int64_t q_row = 0, kv_row = 0, qblk = 0, delta = 0;
+  for (int b = 0; b < a.B; ++b) {
+    int64_t qs = 0, ks = 0, lq = a.Nq, lk = a.Nkv;
+    if (a.varlen) {
+      qs = a.cu_q[b];
+      ks = a.cu_kv[b];
+      lq = a.cu_q[b + 1] - qs;
+      lk = a.cu_kv[b + 1] - ks;
+    }
+    int64_t nqb = (lq + kQBlock - 1) / kQBlock;
+    int64_t kvpad = (lk + kKVPad - 1) / kKVPad * kKVPad;
+    const bool ok = lq >= 0 && lk >= 0 && lq <= a.Nq && lk <= a.Nkv &&
+                    q_row + nqb * kQBlock <= a.lay.q_rows && kv_row + kvpad <= a.lay.kv_rows &&
+                    delta + nqb * kvpad <= a.lay.delta_len;
+    if (!ok) lq = lk = nqb = kvpad = 0;
+    int32_t* r = t + b * kSeqCols;
+    r[kQStart] = (int32_t)qs; r[kQLen] = (int32_t)lq;
+    r[kKVStart] = (int32_t)ks; r[kKVLen] = (int32_t)lk;
+    r[kQRow0] = (int32_t)q_row; r[kKVRow0] = (int32_t)kv_row;
+    r[kQBlk0] = (int32_t)qblk; r[kDelta0] = (int32_t)delta;
+    q_row += nqb * kQBlock;
+    kv_row += kvpad;
+    qblk += nqb;
+    delta += nqb * kvpad;
+  }
+}
+
+// ---- K channel sums and V channel max over one 128-token chunk ---------------------------------
+// grid (chunks, H_kv, B), block D threads: thread c sums channel c over the chunk in token order.
+template <int D, int IN>
+__global__ __launch_bounds__(D) void k_kstats(KArgs a) {
+  const int u = blockIdx.x, g = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+  const Seq s = load_seq(a, b);
+  if (u * kKVPad >= s.kv_len) return;
+  const int j0 = u * kKVPad, j1 = min(s.kv_len, j0 + kKVPad);
+  double part = 0.0;
+  float vmax = 0.0f;
+  for (int j = j0; j < j1; ++j) {
+    part += (double)ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c);
+    vmax = fmaxf(vmax, fabsf(ld_in<IN>(a.v, row_index(a.vs, b, s.kv_start + j, g) + c)));
+  }
+  const int64_t slot = ((int64_t)g * (a.lay.kv_rows / kKVPad) + s.kv_row0 / kKVPad + u) * D + c;
+  ws_ptr<double>(a, a.lay.k_partial)[slot] = part;
+  ws_ptr<float>(a, a.lay.v_partial)[slot] = vmax;
+}
+
+// ---- K mean and V scale: chunks reduced in order -----------------------------------------------
+template <int D>
+__global__ __launch_bounds__(D) void k_kreduce(KArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const Seq s = load_seq(a, b);
+  const int64_t out = ((int64_t)b * a.Hkv + g) * D + c;
+  float kbar = 0.0f, sv = 0.0f, svinv = 0.0f;
+  if (s.kv_len > 0) {
+    const int nch = (s.kv_len + kKVPad - 1) / kKVPad;
+    const int64_t base = ((int64_t)g * (a.lay.kv_rows / kKVPad) + s.kv_row0 / kKVPad) * D + c;
+    double total = 0.0;
+    float amax = 0.0f;
+    for (int u = 0; u < nch; ++u) {
+      total += ws_ptr<double>(a, a.lay.k_partial)[base + (int64_t)u * D];
+      amax = fmaxf(amax, ws_ptr<float>(a, a.lay.v_partial)[base + (int64_t)u * D]);
+    }
+    kbar = (float)(total / (double)s.kv_len);
+    if (amax != 0.0f) {
+      sv = amax / 448.0f;     // V channel amax maps to 448, the largest e4m3 value
+      svinv = 448.0f / amax;
+    }
+  }
+  ws_ptr<float>(a, a.lay.kbar)[out] = kbar;
+  ws_ptr<float>(a, a.lay.sv)[out] = sv;
+  ws_ptr<float>(a, a.lay.sv_inv)[out] = svinv;
+}
+
+// INT4 code of x given the group's inverse scale: round to nearest even, clamp to [-7, 7].
+__device__ inline int int4_code(float x, float inv) {
+  const float y = x * inv;
+  return (int)fminf(7.0f, fmaxf(-7.0f, rintf(y)));
+}
+
+// Packs this lane's codes (C = D/64 consecutive channels per lane) into the row's bytes: byte i
+// holds channel 2i in its low nibble and channel 2i+1 in its high nibble.
+template <int C>
+__device__ inline void store_codes(uint8_t* row, const int (&code)[C], int lane) {
+  if constexpr (C == 2) {
+    row[lane] = (uint8_t)((code[0] & 0xF) | ((code[1] & 0xF) << 4));
+  } else {
+    const int nb = __shfl_down(code[0], 1, 64);
+    if ((lane & 1) == 0) row[lane >> 1] = (uint8_t)((code[0] & 0xF) | ((nb & 0xF) << 4));
+  }
+}
+
+// ---- Q: block mean, per-token INT4 codes -------------------------------------------------------
+// grid (Q blocks, H_q, B), block 256. The block's mean is an fp64 sum over its valid rows in row
+// order; each of the 4 waves then quantizes every 4th row (one scale per token: on gfx950 a lane
+// owns one query column of the S^T = K Q^T MFMA tile, so the per-thread group is one token).
+template <int D, int IN>
+__global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
+  constexpr int C = D / 64;
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const Seq s = load_seq(a, b);
+  if (qb * kQBlock >= s.q_len) return;
+  const int i0 = qb * kQBlock, n = min(kQBlock, s.q_len - i0);
+  __shared__ float qbar[D];
+  if (tid < D) {
+    double sum = 0.0;
+    for (int i = 0; i < n; ++i) sum += (double)ld_in<IN>(a.q, row_index(a.qs, b, s.q_start + i0 + i, h) + tid);
+    const float m = (float)(sum / (double)n);
+    qbar[tid] = m;
+    ws_ptr<float>(a, a.lay.qbar)[((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + tid] = m;
+  }
+  __syncthreads();
+  uint8_t* qcode = ws_ptr<uint8_t>(a, a.lay.qcode);
+  float* sq = ws_ptr<float>(a, a.lay.sq);
+  for (int r = wave; r < kQBlock; r += 4) {
+    const int64_t prow = (int64_t)h * a.lay.q_rows + s.q_row0 + i0 + r;
+    int code[C];
+    float scale = 0.0f;
+    if (r < n) {
+      const int64_t base = row_index(a.qs, b, s.q_start + i0 + r, h);
+      float qt[C];
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        const int c = lane * C + e;
+        qt[e] = ld_in<IN>(a.q, base + c) - qbar[c];
+        amax = fmaxf(amax, fabsf(qt[e]));
+      }
+      amax = wave_max(amax);
+      const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
+      scale = amax == 0.0f ? 0.0f : amax / 7.0f;
+#pragma unroll
+      for (int e = 0; e < C; ++e) code[e] = int4_code(qt[e], inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < C; ++e) code[e] = 0;
+    }
+    store_codes<C>(qcode + prow * (D / 2), code, lane);
+    if (lane == 0) sq[prow] = scale;
+  }
+}
+
+// Key index (within a 64-key tile) held in slot s of lane half h: the S^T accumulator of the
+// 32x32 MFMA gives lane half h the rows 8*(r/4) + 4*h + r%4 of each 32-key subtile.
+__device__ inline int tile_key(int h, int s) { return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * h + (s & 3); }
+
+// ---- K: per-16-key-group INT4 codes; V: FP8 codes in the attention kernel's tile layout -------
+// grid (64-key tiles, H_kv, B), block 256. Wave w quantizes group w of the tile: the 16 keys of
+// 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half owns).
+template <int D, int IN>
+__global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
+  constexpr int C = D / 64;
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const Seq s = load_seq(a, b);
+  const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
+  if (t * kKVTile >= kvpad) return;
+  __shared__ float kbar[D], svinv[D];
+  __shared__ float vt[kKVTile][D + 1];
+  const int64_t sidx = ((int64_t)b * a.Hkv + g) * D;
+  if (tid < D) {
+    kbar[tid] = ws_ptr<float>(a, a.lay.kbar)[sidx + tid];
+    svinv[tid] = ws_ptr<float>(a, a.lay.sv_inv)[sidx + tid];
+  }
+  __syncthreads();
+  // K group of this wave
+  {
+    const int half = wave & 1, sub = wave >> 1;
+    float kt[16][C];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = t * kKVTile + 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);
+#pragma unroll
+      for (int x = 0; x < C; ++x) {
+        const int c = lane * C + x;
+        float val = 0.0f;
+        if (j < s.kv_len) val = ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c];
+        kt[e][x] = val;
+        amax = fmaxf(amax, fabsf(val));
+      }
+    }
+    amax = wave_max(amax);
+    const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
+    const float scale = amax == 0.0f ? 0.0f : amax / 7.0f;
+    uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = t * kKVTile + 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);
+      int code[C];
+#pragma unroll
+      for (int x = 0; x < C; ++x) code[x] = int4_code(kt[e][x], inv);
+      store_codes<C>(kcode + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (D / 2), code, lane);
+    }
+    if (lane == 0)
+      ws_ptr<float>(a, a.lay.sk)[(int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16 + 4 * t + wave] = scale;
+  }
+  // V tile, scaled per channel, staged in LDS
+  for (int idx = tid; idx < kKVTile * D; idx += 256) {
+    const int key = idx / D, c = idx % D;
+    const int j = t * kKVTile + key;
+    float val = 0.0f;
+    if (j < s.kv_len) val = ld_in<IN>(a.v, row_index(a.vs, b, s.kv_start + j, g) + c) * svinv[c];
+    vt[key][c] = val;
+  }
+  __syncthreads();
+  uint8_t* v8 = ws_ptr<uint8_t>(a, a.lay.v8) +
+                ((int64_t)g * (a.lay.kv_rows / kKVTile) + s.kv_row0 / kKVTile + t) * (kKVTile * D);
+  for (int p = tid; p < 2 * D; p += 256) {
+    const int c = p >> 1, h = p & 1;
+    int w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int s0 = 4 * q;
+      int x = cvt_fp8x2(vt[tile_key(h, s0)][c], vt[tile_key(h, s0 + 1)][c], 0, false);
+      w[q] = cvt_fp8x2(vt[tile_key(h, s0 + 2)][c], vt[tile_key(h, s0 + 3)][c], x, true);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(v8 + (int64_t)p * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// ---- correction table: delta[qb][j] = (qbar_qb . ktilde_j) * sm_scale * log2(e) ---------------
+// Q smoothing removes each block's mean from the INT4 product; this adds back its exact share
+// (fp64 sum in channel order, one rounding to f32). grid (64-key tiles, H_kv, B), block 256:
+// lanes are keys, waves take the (q head, Q block) pairs of the kv head in turn. Entries a causal
+// mask hides from every row of the block are written as 0.
+template <int D, int IN>
+__global__ __launch_bounds__(256) void k_delta(KArgs a) {
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const Seq s = load_seq(a, b);
+  const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
+  if (t * kKVTile >= kvpad) return;
+  __shared__ float kt[kKVTile][D + 1];
+  const float* kbar = ws_ptr<float>(a, a.lay.kbar) + ((int64_t)b * a.Hkv + g) * D;
+  for (int idx = tid; idx < kKVTile * D; idx += 256) {
+    const int key = idx / D, c = idx % D;
+    const int j = t * kKVTile + key;
+    float val = 0.0f;
+    if (j < s.kv_len) val = ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c];
+    kt[key][c] = val;
+  }
+  __syncthreads();
+  const int grp = a.Hq / a.Hkv;
+  const int nqb = (s.q_len + kQBlock - 1) / kQBlock;
+  const int j = t * kKVTile + lane;
+  const double L = (double)a.L;
+  float* delta = ws_ptr<float>(a, a.lay.delta);
+  for (int pair = wave; pair < grp * nqb; pair += 4) {
+    const int h = g * grp + pair / nqb, qb = pair % nqb;
+    const float* qbar = ws_ptr<float>(a, a.lay.qbar) + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D;
+    int jmax = s.kv_len - 1;
+    if (a.causal) jmax = min(jmax, min(s.q_len, (qb + 1) * kQBlock) - 1 + (s.kv_len - s.q_len));
+    float val = 0.0f;
+    if (j <= jmax) {
+      double acc = 0.0;
+      for (int c = 0; c < D; ++c) acc += (double)qbar[c] * (double)kt[lane][c];
+      val = (float)(acc * L);
+    }
+    delta[(int64_t)h * a.lay.delta_len + s.delta0 + (int64_t)qb * kvpad + j] = val;
+  }
+}
+
+template <int D, int IN>
+int launch_all(const KArgs& a, hipStream_t st) {
+  const int nch = (a.Nkv + kKVPad - 1) / kKVPad;
+  const int nqb = (a.Nq + kQBlock - 1) / kQBlock;
+  const int ntile = nch * (kKVPad / kKVTile);
+  k_plan<<<1, 64, 0, st>>>(a);
+  k_kstats<D, IN><<<dim3(nch, a.Hkv, a.B), D, 0, st>>>(a);
+  k_kreduce<D><<<dim3(a.Hkv, a.B), D, 0, st>>>(a);
+  k_quant_q<D, IN><<<dim3(nqb, a.Hq, a.B), 256, 0, st>>>(a);
+  k_quant_kv<D, IN><<<dim3(ntile, a.Hkv, a.B), 256, 0, st>>>(a);
+  k_delta<D, IN><<<dim3(ntile, a.Hkv, a.B), 256, 0, st>>>(a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_prepass(const KArgs& a, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (a.d == 64) return a.in_dtype == SAGE2_BF16 ? launch_all<64, SAGE2_BF16>(a, st) : launch_all<64, SAGE2_F16>(a, st);
+  return a.in_dtype == SAGE2_BF16 ? launch_all<128, SAGE2_BF16>(a, st) : launch_all<128, SAGE2_F16>(a, st);
+}
+
+}  // namespace sage2

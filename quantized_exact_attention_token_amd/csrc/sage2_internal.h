@@ -1,0 +1,39 @@
+// Internal interface between the host library (argument checks, workspace layout) and the HIP
+// launchers. Not installed; the public ABI is include/sage2.h.
+#pragma once
+
+#include <cstdint>
+
+#include "sage2.h"
+
+namespace sage2 {
+
+constexpr int kQBlock = 128;   // Q smoothing block = attention workgroup Q tile (tokens)
+constexpr int kKVPad = 128;    // per-sequence K/V row padding (K mean chunk size)
+constexpr int kKVTile = 64;    // attention KV tile (keys)
+constexpr int kSeqCols = 8;    // int32 columns of a sequence-table row
+
+// Columns of the per-sequence table the plan kernel writes into the workspace.
+enum SeqCol { kQStart = 0, kQLen, kKVStart, kKVLen, kQRow0, kKVRow0, kQBlk0, kDelta0 };
+
+// Everything a kernel needs, passed by value.
+struct KArgs {
+  int32_t B, Hq, Hkv, Nq, Nkv, d, causal, in_dtype, out_dtype, varlen;
+  float L;  // sm_scale * log2(e) in f32: logits are carried in base-2 units
+  const void *q, *k, *v;
+  void* o;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  const int32_t *cu_q, *cu_kv;
+  char* ws;
+  sage2_ws_layout lay;
+  // debug dump
+  int32_t dbg_q0, dbg_qn;
+  int32_t* dbg_out;
+};
+
+// Launchers (defined in the .hip files). Return hipSuccess as 0, else the HIP error code.
+int launch_prepass(const KArgs& a, void* stream);
+int launch_attn(const KArgs& a, void* stream);
+int launch_debug_qk(const KArgs& a, void* stream);
+
+}  // namespace sage2

@@ -1,0 +1,182 @@
+"""Shared helpers for the GPU parity tests and the benchmark: run the HIP path through the C ABI,
+decode the workspace into the oracle's canonical arrays, and compare with the oracle.
+
+Decoding only reorders bytes (nibble unpacking, the V tile permutation); it does no arithmetic of
+the method.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import quantized_exact_attention_token_amd as sage2
+from quantized_exact_attention_token_amd import workloads as W
+
+OUT_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+class GpuRun:
+    """Inputs on the device, params, workspace, output."""
+
+    def __init__(self, w: W.Workload, out_dtype=None, layout: str = "bnhd", device="cuda"):
+        self.w = w
+        q, k, v, cu = W.generate(w)
+        self.q_cpu, self.k_cpu, self.v_cpu, self.cu_cpu = q, k, v, cu
+        dev = torch.device(device)
+        if layout == "bhnd" and cu is None:  # same values, [B, H, N, d] storage seen through strides
+            q, k, v = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        odt = out_dtype or w.dtype
+        self.o = torch.full(self.q.shape, float("nan"), dtype=odt, device=dev)
+        self.cu = None if cu is None else cu.to(dev)
+        self.p = sage2.make_params(self.q, self.k, self.v, self.o, w.causal,
+                                   cu_seqlens_q=self.cu, cu_seqlens_kv=self.cu,
+                                   max_seqlen_q=w.Nq if cu is not None else None,
+                                   max_seqlen_kv=w.Nkv if cu is not None else None)
+        self.ws = torch.empty(sage2.workspace_size(self.p), dtype=torch.uint8, device=dev)
+        self.lay = sage2.workspace_layout(self.p)
+
+    def prepass(self):
+        sage2.quantize_smooth(self.p, self.q, self.k, self.v, self.ws)
+
+    def attn(self):
+        sage2.attn_fwd(self.p, self.ws, self.o)
+
+    def run(self):
+        self.prepass()
+        self.attn()
+        torch.cuda.synchronize()
+        return self.o
+
+    def debug_qk(self, q_begin, q_count):
+        w = self.w
+        s = torch.full((self.p.B, w.Hq, q_count, self.p.N_kv), -(2 ** 31), dtype=torch.int32,
+                       device=self.q.device)
+        sage2.debug_qk_i32(self.p, self.ws, q_begin, q_count, s)
+        torch.cuda.synchronize()
+        return s.cpu().numpy()
+
+    # ---- workspace decoding -------------------------------------------------------------------
+    def ws_host(self):
+        torch.cuda.synchronize()
+        return self.ws.cpu().numpy()
+
+    def sequences(self):
+        """[(q_len, kv_len)] per sequence."""
+        if self.cu_cpu is None:
+            return [(self.w.Nq, self.w.Nkv)] * self.w.B
+        cu = self.cu_cpu.numpy()
+        return [(int(cu[i + 1] - cu[i]),) * 2 for i in range(len(cu) - 1)]
+
+    def decode(self, ws: np.ndarray, b: int):
+        """Canonical pre-pass outputs of sequence b, shaped like the oracle's."""
+        lay, w = self.lay, self.w
+        d, Hq, Hkv = w.d, w.Hq, w.Hkv
+        tab = ws[lay.seq_table:lay.seq_table + 4 * 8 * self.p.B].view(np.int32).reshape(-1, 8)
+        qs, lq, ks, lk, qrow0, kvrow0, qblk0, delta0 = (int(x) for x in tab[b])
+        nqb = (lq + 127) // 128
+        kvpad = (lk + 127) // 128 * 128
+
+        def arr(off, dtype, count):
+            nbytes = count * np.dtype(dtype).itemsize
+            return ws[off:off + nbytes].view(dtype)
+
+        def unpack(raw):  # [..., d/2] u8 -> [..., d] int8
+            lo = (raw & 0xF).astype(np.int8)
+            hi = (raw >> 4).astype(np.int8)
+            lo = np.where(lo >= 8, lo - 16, lo).astype(np.int8)
+            hi = np.where(hi >= 8, hi - 16, hi).astype(np.int8)
+            out = np.empty(raw.shape[:-1] + (raw.shape[-1] * 2,), np.int8)
+            out[..., 0::2], out[..., 1::2] = lo, hi
+            return out
+
+        out = {"table": (qs, lq, ks, lk, qrow0, kvrow0, qblk0, delta0)}
+        out["kbar"] = arr(lay.kbar, np.float32, self.p.B * Hkv * d).reshape(self.p.B, Hkv, d)[b]
+        out["sv"] = arr(lay.sv, np.float32, self.p.B * Hkv * d).reshape(self.p.B, Hkv, d)[b]
+        qbar = arr(lay.qbar, np.float32, Hq * lay.q_blocks * d).reshape(Hq, lay.q_blocks, d)
+        out["qbar"] = qbar[:, qblk0:qblk0 + nqb]
+        qc = arr(lay.qcode, np.uint8, Hq * lay.q_rows * d // 2).reshape(Hq, lay.q_rows, d // 2)
+        out["qcode"] = unpack(qc[:, qrow0:qrow0 + lq])
+        out["qcode_pad"] = unpack(qc[:, qrow0 + lq:qrow0 + nqb * 128])
+        sq = arr(lay.sq, np.float32, Hq * lay.q_rows).reshape(Hq, lay.q_rows)
+        out["sq"] = sq[:, qrow0:qrow0 + lq]
+        kc = arr(lay.kcode, np.uint8, Hkv * lay.kv_rows * d // 2).reshape(Hkv, lay.kv_rows, d // 2)
+        out["kcode"] = unpack(kc[:, kvrow0:kvrow0 + lk])
+        sk = arr(lay.sk, np.float32, Hkv * lay.kv_rows // 16).reshape(Hkv, lay.kv_rows // 16)
+        out["sk"] = sk[:, kvrow0 // 16:kvrow0 // 16 + 2 * ((lk + 31) // 32)]
+        v8 = arr(lay.v8, np.uint8, Hkv * lay.kv_rows * d).reshape(Hkv, lay.kv_rows // 64, d, 2, 32)
+        v8 = v8[:, kvrow0 // 64:(kvrow0 + kvpad) // 64]
+        canon = np.empty((Hkv, v8.shape[1] * 64, d), np.uint8)
+        for h in range(2):
+            for s in range(32):
+                key = 32 * (s // 16) + 8 * ((s % 16) // 4) + 4 * h + s % 4
+                canon[:, key::64, :] = v8[:, :, :, h, s]
+        out["v8"] = canon[:, :lk]
+        dl = arr(lay.delta, np.float32, Hq * lay.delta_len).reshape(Hq, lay.delta_len)
+        out["delta"] = dl[:, delta0:delta0 + nqb * kvpad].reshape(Hq, nqb, kvpad)[:, :, :lk]
+        return out
+
+    def seq_inputs(self, b: int, heads=None):
+        """Head-major float32 inputs of sequence b for the oracle ([Hq, L, d], [Hkv, L, d]);
+        `heads` = (first kv head, number of kv heads) limits them to a kv-head group range."""
+        if self.cu_cpu is None:
+            q, k, v = self.q_cpu[b], self.k_cpu[b], self.v_cpu[b]
+        else:
+            s, e = int(self.cu_cpu[b]), int(self.cu_cpu[b + 1])
+            q, k, v = self.q_cpu[s:e], self.k_cpu[s:e], self.v_cpu[s:e]
+        if heads is not None:
+            g0, ng = heads
+            grp = self.w.Hq // self.w.Hkv
+            q = q[:, g0 * grp:(g0 + ng) * grp]
+            k, v = k[:, g0:g0 + ng], v[:, g0:g0 + ng]
+        f = lambda t: t.float().permute(1, 0, 2).contiguous().numpy()
+        return f(q), f(k), f(v)
+
+    def out_seq(self, b: int):
+        """GPU output of sequence b as float64 [Hq, L, d]."""
+        o = self.o.float().cpu()
+        if self.cu_cpu is None:
+            o = o[b]
+        else:
+            o = o[int(self.cu_cpu[b]):int(self.cu_cpu[b + 1])]
+        return o.permute(1, 0, 2).double().numpy()
+
+
+def half_ulp(ref: np.ndarray, dtype) -> np.ndarray:
+    """Half a unit in the last place of `dtype` at |ref|: the rounding the output format itself
+    adds to any correctly computed value."""
+    if dtype == torch.float32:
+        mant, emin = 23, -126
+    elif dtype == torch.bfloat16:
+        mant, emin = 7, -126
+    else:
+        mant, emin = 10, -14
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** emin)))
+    return 0.5 * 2.0 ** (e - mant)
+
+
+def cos(a, b) -> float:
+    a, b = np.ravel(a).astype(np.float64), np.ravel(b).astype(np.float64)
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    if na == 0 and nb == 0:
+        return 1.0
+    return float(a @ b / (na * nb))
+
+
+MAX_ABS_TOL = 1e-2   # output max-abs error against the oracle's quantized pipeline
+COS_TOL = 0.9999     # cosine similarity against the oracle's quantized pipeline
+
+
+def check_output(gpu: np.ndarray, ref: np.ndarray, allow: np.ndarray, dtype, what=""):
+    """Element-wise |gpu - ref| <= 1e-2 + allowance for ambiguous FP8 roundings of P~ + half an
+    ulp of the output format; cos >= 0.9999. Returns a dict of the measured figures."""
+    err = np.abs(gpu - ref)
+    tol = MAX_ABS_TOL + allow + half_ulp(ref, dtype)
+    bad = err > tol
+    c = cos(gpu, ref)
+    info = dict(max_abs=float(err.max()) if err.size else 0.0, cos=c,
+                n_bad=int(bad.sum()), allow_max=float(allow.max()) if allow.size else 0.0)
+    assert not np.isnan(gpu).any(), f"{what}: NaN in GPU output"
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, worst {err.max():.3e} {info}"
+    assert c >= COS_TOL, f"{what}: cos {c} < {COS_TOL}"
+    return info
