@@ -75,13 +75,87 @@ __device__ inline void store4(char* dst, float a, float b, float c, float d) {
   }
 }
 
-// One workgroup = one (sequence, q head, 128-query block); 4 waves x 32 queries.
-// Causal grids run the longest blocks (highest qb) first.
+// Workgroup -> (q head, 128-query block) of one sequence. Work is ordered longest causal block
+// first, and within a block index the q heads that share a kv head are consecutive; dispatches go
+// round-robin over the 8 XCDs, so each run of `grp` consecutive work items is placed on one XCD
+// (its q heads then read the same K/V through that XCD's L2).
+__device__ inline void decode_work(int L, int nqb, int Hq, int grp, int* qb, int* h) {
+  const int total = nqb * Hq;
+  const int round = 8 * grp;
+  int w = L;
+  if (L < total / round * round) w = (L / round) * round + (L % 8) * grp + (L / 8) % grp;
+  *qb = nqb - 1 - w / Hq;
+  *h = w % Hq;
+}
+
+// LDS staging of one 64-key tile: K as unpacked i8 operands (16*code), V in its tile layout with
+// padded channel rows, the tile's 64 correction values and its 4 K group scales.
+template <int D>
+struct Stage {
+  static constexpr int KROW = D + 16;          // bytes per K row (16 bytes of padding)
+  static constexpr int VCH = 80;               // bytes per V channel (64 keys + 16 padding)
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 64 * KROW;
+  static constexpr int D_OFF = V_OFF + D * VCH;
+  static constexpr int S_OFF = D_OFF + 64 * 4;
+  static constexpr int BYTES = S_OFF + 16;
+  static constexpr int K_THREADS = 64 * D / 32;  // 16 packed bytes per thread
+  static constexpr int V_BYTES = 64 * D / 256;   // per thread
+};
+
+template <int D>
+struct TileRegs {
+  uint4 k;
+  uint4 v[Stage<D>::V_BYTES / 16];
+  uint4 dl;
+};
+
+template <int D>
+__device__ inline void tile_load(TileRegs<D>& r, int tid, int t, const uint8_t* kcode,
+                                 const uint8_t* v8, const float* drow, const float* skp) {
+  using S = Stage<D>;
+  if (tid < S::K_THREADS) {
+    const int key = tid / (D / 32), part = tid % (D / 32);
+    r.k = *reinterpret_cast<const uint4*>(kcode + (int64_t)(t * 64 + key) * (D / 2) + part * 16);
+  }
+  const uint4* vs = reinterpret_cast<const uint4*>(v8 + (int64_t)t * 64 * D + tid * S::V_BYTES);
+#pragma unroll
+  for (int u = 0; u < S::V_BYTES / 16; ++u) r.v[u] = vs[u];
+  if (tid < 16) r.dl = *reinterpret_cast<const uint4*>(drow + t * 64 + tid * 4);
+  else if (tid == 16) r.dl = *reinterpret_cast<const uint4*>(skp + 4 * t);
+}
+
+template <int D>
+__device__ inline void tile_store(const TileRegs<D>& r, int tid, uint8_t* st) {
+  using S = Stage<D>;
+  if (tid < S::K_THREADS) {
+    const int key = tid / (D / 32), part = tid % (D / 32);
+    const v4i lo = unpack16(r.k.x, r.k.y), hi = unpack16(r.k.z, r.k.w);
+    uint4* dst = reinterpret_cast<uint4*>(st + S::K_OFF + key * S::KROW + part * 32);
+    dst[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    dst[1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
+  const int o = tid * S::V_BYTES;
+  uint4* vd = reinterpret_cast<uint4*>(st + S::V_OFF + (o / 64) * S::VCH + (o % 64));
+#pragma unroll
+  for (int u = 0; u < S::V_BYTES / 16; ++u) vd[u] = r.v[u];
+  if (tid < 16) *reinterpret_cast<uint4*>(st + S::D_OFF + tid * 16) = r.dl;
+  else if (tid == 16) *reinterpret_cast<uint4*>(st + S::S_OFF) = r.dl;
+}
+
+// One workgroup = one (sequence, q head, 128-query block); 4 waves x 32 queries. K/V tiles of 64
+// keys are staged once per workgroup in LDS (double-buffered, next tile's global loads in flight
+// while the current tile is computed).
 template <int D, int CAUSAL, int OUT>
-__global__ __launch_bounds__(256) void k_attn(KArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   constexpr int NCH = D / 32;
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  using S = Stage<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BYTES];
+
+  const int b = blockIdx.y;
+  const int nqb_grid = (a.Nq + kQBlock - 1) / kQBlock;
+  int qb, h;
+  decode_work(blockIdx.x, nqb_grid, a.Hq, a.Hq / a.Hkv, &qb, &h);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
   const Seq s = load_seq(a, b);
   if (qb * kQBlock >= s.q_len) return;
@@ -89,17 +163,22 @@ __global__ __launch_bounds__(256) void k_attn(KArgs a) {
   const int i = qb * kQBlock + 32 * wave + n;  // this lane's query row within the sequence
   const int64_t prow = (int64_t)h * a.lay.q_rows + s.q_row0 + i;
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
+  const int koff = s.kv_len - s.q_len;
 
   v4i qop[NCH];
   load_codes<D>(ws_ptr<uint8_t>(a, a.lay.qcode) + prow * (D / 2), hh, qop);
   // (s_q * L) * 2^-8: the 2^-8 undoes the 16*16 carried by the two operands (exact).
   const float cq = (ws_ptr<float>(a, a.lay.sq)[prow] * a.L) * 0.00390625f;
 
-  int ntile = (s.kv_len + kKVTile - 1) / kKVTile;
-  const int koff = s.kv_len - s.q_len;
+  // tiles for the workgroup (all waves stage) and for this wave (causal: up to its last row)
+  int nt = (s.kv_len + kKVTile - 1) / kKVTile;
+  int nt_w = nt;
+  const int wave_row0 = qb * kQBlock + 32 * wave;
   if (CAUSAL) {
-    const int kmax = min(s.q_len, qb * kQBlock + 32 * wave + 32) - 1 + koff;
-    ntile = kmax < 0 ? 0 : min(ntile, kmax / kKVTile + 1);
+    const int kmax = min(s.q_len, qb * kQBlock + kQBlock) - 1 + koff;
+    nt = kmax < 0 ? 0 : min(nt, kmax / kKVTile + 1);
+    const int kmax_w = min(s.q_len, wave_row0 + 32) - 1 + koff;
+    nt_w = kmax_w < 0 ? 0 : min(nt_w, kmax_w / kKVTile + 1);
   }
   const uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * (D / 2);
   const float* skp = ws_ptr<float>(a, a.lay.sk) + (int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16;
@@ -112,63 +191,83 @@ __global__ __launch_bounds__(256) void k_attn(KArgs a) {
 #pragma unroll
   for (int cb = 0; cb < NCH; ++cb) o[cb] = v16f{};
 
-  for (int t = 0; t < ntile; ++t) {
-    float x[32];
+  TileRegs<D> tr;
+  if (nt > 0) {
+    tile_load<D>(tr, tid, 0, kcode, v8, drow, skp);
+    tile_store<D>(tr, tid, smem);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < nt; ++t) {
+    uint8_t* st = smem + (t & 1) * S::BYTES;
+    const bool more = t + 1 < nt;
+    if (more) tile_load<D>(tr, tid, t + 1, kcode, v8, drow, skp);
+    if (t < nt_w) {
+      // the wave needs masking only on a ragged last tile or where the causal edge crosses
+      const bool need_mask = (t * kKVTile + kKVTile > s.kv_len) ||
+                             (CAUSAL && t * kKVTile + kKVTile - 1 > wave_row0 + koff);
+      const float* sks = reinterpret_cast<const float*>(st + S::S_OFF);
+      float x[32];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int key0 = t * kKVTile + 32 * st;
-      v4i kop[NCH];
-      load_codes<D>(kcode + (int64_t)(key0 + n) * (D / 2), hh, kop);
-      v16i acc = v16i{};
+      for (int sub = 0; sub < 2; ++sub) {
+        const uint8_t* krow = st + S::K_OFF + (32 * sub + n) * S::KROW + hh * (D / 2);
+        v16i acc = v16i{};
 #pragma unroll
-      for (int cb = 0; cb < NCH; ++cb) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[cb], qop[cb], acc, 0, 0, 0);
-      const float cs = cq * skp[2 * (key0 / 32) + hh];
+        for (int cb = 0; cb < NCH; ++cb) {
+          const v4i kop = *reinterpret_cast<const v4i*>(krow + cb * 16);
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[cb], acc, 0, 0, 0);
+        }
+        const float cs = cq * sks[2 * sub + hh];
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 dl = *reinterpret_cast<const float4*>(drow + key0 + 8 * a4 + 4 * hh);
-        const float dv[4] = {dl.x, dl.y, dl.z, dl.w};
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const float4 dl = *reinterpret_cast<const float4*>(st + S::D_OFF + (32 * sub + 8 * a4 + 4 * hh) * 4);
+          const float dv[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * a4 + e;
-          const int key = key0 + 8 * a4 + 4 * hh + e;
-          const float xv = __builtin_fmaf((float)acc[r], cs, dv[e]);
-          const bool vis = key < s.kv_len && (!CAUSAL || key <= i + koff);
-          x[16 * st + r] = vis ? xv : kNegInf;
+          for (int e = 0; e < 4; ++e) x[16 * sub + 4 * a4 + e] = __builtin_fmaf((float)acc[4 * a4 + e], cs, dv[e]);
         }
       }
+      if (need_mask) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const int key = t * kKVTile + 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * hh + (k & 3);
+          const bool vis = key < s.kv_len && (!CAUSAL || key <= i + koff);
+          x[k] = vis ? x[k] : kNegInf;
+        }
+      }
+      float mt = x[0];
+#pragma unroll
+      for (int k = 1; k < 32; ++k) mt = fmaxf(mt, x[k]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mnew = fmaxf(m, mt);
+      const float alpha = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
+      const float mb = (mnew == kNegInf) ? 0.0f : mnew - kLog2_448;
+      float ps = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        x[k] = __builtin_amdgcn_exp2f(x[k] - mb);
+        ps += x[k];
+      }
+      lsum = alpha * lsum + ps;
+      v8i pop;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int w = cvt_fp8x2(x[4 * q], x[4 * q + 1], 0, false);
+        pop[q] = cvt_fp8x2(x[4 * q + 2], x[4 * q + 3], w, true);
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCH; ++cb) {
+        const uint8_t* vrow = st + S::V_OFF + (32 * cb + n) * S::VCH + hh * 32;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(vrow);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + 16);
+        const v8i vop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        const v16f inner = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, v16f{}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(alpha, o[cb][r], inner[r]);
+      }
+      m = mnew;
     }
-    float mt = x[0];
-#pragma unroll
-    for (int k = 1; k < 32; ++k) mt = fmaxf(mt, x[k]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mnew = fmaxf(m, mt);
-    const float alpha = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
-    const float mb = (mnew == kNegInf) ? 0.0f : mnew - kLog2_448;
-    float p[32];
-    float ps = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      p[k] = __builtin_amdgcn_exp2f(x[k] - mb);
-      ps += p[k];
-    }
-    lsum = alpha * lsum + ps;
-    v8i pop;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int w = cvt_fp8x2(p[4 * q], p[4 * q + 1], 0, false);
-      pop[q] = cvt_fp8x2(p[4 * q + 2], p[4 * q + 3], w, true);
-    }
-    const uint8_t* vt = v8 + (int64_t)t * kKVTile * D;
-#pragma unroll
-    for (int cb = 0; cb < NCH; ++cb) {
-      const uint4* src = reinterpret_cast<const uint4*>(vt + ((32 * cb + n) * 2 + hh) * 32);
-      const uint4 v0 = src[0], v1 = src[1];
-      const v8i vop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      const v16f inner = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, v16f{}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(alpha, o[cb][r], inner[r]);
-    }
-    m = mnew;
+    if (more) tile_store<D>(tr, tid, smem + ((t + 1) & 1) * S::BYTES);
+    __syncthreads();
   }
 
   lsum += __shfl_xor(lsum, 32, 64);
@@ -234,7 +333,7 @@ __global__ __launch_bounds__(256) void k_debug_qk(KArgs a) {
 
 template <int D, int CAUSAL>
 int launch_attn_d(const KArgs& a, hipStream_t st) {
-  const dim3 grid((a.Nq + kQBlock - 1) / kQBlock, a.Hq, a.B);
+  const dim3 grid((a.Nq + kQBlock - 1) / kQBlock * a.Hq, a.B);
   switch (a.out_dtype) {
     case SAGE2_F32: k_attn<D, CAUSAL, SAGE2_F32><<<grid, 256, 0, st>>>(a); break;
     case SAGE2_BF16: k_attn<D, CAUSAL, SAGE2_BF16><<<grid, 256, 0, st>>>(a); break;
