@@ -250,10 +250,12 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
 // ---- correction table: delta[qb][j] = (qbar_qb . ktilde_j) * sm_scale * log2(e) ---------------
 // Q smoothing removes each block's mean from the INT4 product; this adds back its exact share
 // (fp64 sum in channel order, one rounding to f32). grid (64-key tiles, H_kv, B), block 256:
-// lanes are keys, waves take the (q head, Q block) pairs of the kv head in turn. Entries a causal
-// mask hides from every row of the block are written as 0.
+// lanes are keys; each wave takes NP (q head, Q block) pairs of the kv head at a time and runs
+// their NP sums side by side (independent fp64 chains, each still in channel order). Entries a
+// causal mask hides from every row of the block are written as 0.
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_delta(KArgs a) {
+  constexpr int NP = 4;
   const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seq s = load_seq(a, b);
@@ -271,21 +273,38 @@ __global__ __launch_bounds__(256) void k_delta(KArgs a) {
   __syncthreads();
   const int grp = a.Hq / a.Hkv;
   const int nqb = (s.q_len + kQBlock - 1) / kQBlock;
+  const int npairs = grp * nqb;
   const int j = t * kKVTile + lane;
   const double L = (double)a.L;
   float* delta = ws_ptr<float>(a, a.lay.delta);
-  for (int pair = wave; pair < grp * nqb; pair += 4) {
-    const int h = g * grp + pair / nqb, qb = pair % nqb;
-    const float* qbar = ws_ptr<float>(a, a.lay.qbar) + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D;
-    int jmax = s.kv_len - 1;
-    if (a.causal) jmax = min(jmax, min(s.q_len, (qb + 1) * kQBlock) - 1 + (s.kv_len - s.q_len));
-    float val = 0.0f;
-    if (j <= jmax) {
-      double acc = 0.0;
-      for (int c = 0; c < D; ++c) acc += (double)qbar[c] * (double)kt[lane][c];
-      val = (float)(acc * L);
+  const float* qbar_all = ws_ptr<float>(a, a.lay.qbar);
+  for (int p0 = wave * NP; p0 < npairs; p0 += 4 * NP) {
+    const float* qb_ptr[NP];
+    int64_t out[NP];
+    bool live[NP];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int pair = min(p0 + u, npairs - 1);
+      const int h = g * grp + pair / nqb, qb = pair % nqb;
+      qb_ptr[u] = qbar_all + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D;
+      out[u] = (int64_t)h * a.lay.delta_len + s.delta0 + (int64_t)qb * kvpad + j;
+      int jmax = s.kv_len - 1;
+      if (a.causal) jmax = min(jmax, min(s.q_len, (qb + 1) * kQBlock) - 1 + (s.kv_len - s.q_len));
+      live[u] = p0 + u < npairs && j <= jmax;
     }
-    delta[(int64_t)h * a.lay.delta_len + s.delta0 + (int64_t)qb * kvpad + j] = val;
+    double acc[NP];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) acc[u] = 0.0;
+    if (live[0] || live[1] || live[2] || live[3]) {
+      for (int c = 0; c < D; ++c) {
+        const double kv = (double)kt[lane][c];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) acc[u] += (double)qb_ptr[u][c] * kv;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NP; ++u)
+      if (p0 + u < npairs) delta[out[u]] = live[u] ? (float)(acc[u] * L) : 0.0f;
   }
 }
 
