@@ -88,9 +88,11 @@ typedef struct {
  *   kbar       f32   [B][H_kv][d]             K channel means
  *   sv, sv_inv f32   [B][H_kv][d]             V channel scale amax/448 and its inverse 448/amax
  *   qbar       f32   [H_q][q_blocks][d]       Q block means
- *   qcode      u8    [H_q][q_rows][d/2]       INT4 codes, channel 2i in the low nibble of byte i
+ *   qcode      u8    [H_q][q_rows][3d/4]      INT4 codes in 6-bit e2m3 fields (the gfx950 fp6
+ *                                             MFMA operand format, exact for -7..7): channel c at
+ *                                             bits [6c, 6c+6) of the row, little-endian
  *   sq         f32   [H_q][q_rows]            per-token Q scale
- *   kcode      u8    [H_kv][kv_rows][d/2]     INT4 codes, same nibble order
+ *   kcode      u8    [H_kv][kv_rows][3d/4]    INT4 codes, same encoding
  *   sk         f32   [H_kv][kv_rows/16]       K scale of group 2*(j/32) + bit 2 of j
  *   v8         u8    [H_kv][kv_rows/64][d][2][32]  FP8 e4m3 codes of V*sv_inv; within a 64-key
  *                                             tile, channel c, half h, slot s holds key

@@ -144,7 +144,7 @@ def logits(z: Quantized, causal: bool, rows=None, nthreads: int = 0):
     return x
 
 
-def attn_quant(z: Quantized, causal: bool, rows=None, bn: int = 64, flags: int = 0,
+def attn_quant(z: Quantized, causal: bool, rows=None, bn: int = 128, flags: int = 0,
                nthreads: int = 0):
     """Returns (out, allow): [Hq, nrows, d] float64 each. `allow` bounds the effect of FP8
     roundings of P~ that sit within the kernel's arithmetic error of a rounding boundary."""

@@ -8,19 +8,23 @@
 // periodic FP32 foldback) and "Per-Thread INT4 Geometry" (scale groups follow thread ownership).
 //
 // gfx950 form of the method:
-//  - S^T = K Q^T on v_mfma_i32_32x32x32_i8. A lane owns one query (column) and, in each 32-key
-//    subtile, the 16 keys whose index has bit 2 equal to its half-wave index. So one Q scale and one
-//    K scale per lane and subtile dequantize all 16 accumulators: the per-thread scale groups.
-//    INT4 codes are carried as 16*code in the i8 operands (a nibble mask unpacks them), so the
-//    INT32 accumulator holds 256*S exactly.
+//  - S^T = K Q^T on the 32x32 MFMA. A lane owns one query (column) and, in each 32-key subtile,
+//    the 16 keys whose index has bit 2 equal to its half-wave index. So one Q scale and one K scale
+//    per lane and subtile dequantize all 16 accumulators: the per-thread scale groups.
+//    gfx950 has no INT4 MFMA. The INT4 codes ride in 6-bit e2m3 fields, in which every integer in
+//    [-7, 7] is exact, on v_mfma_scale_f32_32x32x64_f8f6f4 (fp6 x fp6, unit scales): the products
+//    are small integers and the f32 accumulation of them is exact (|S| <= 49 d), so the accumulator
+//    holds the INT32 product S exactly, at twice the K depth per instruction of the i8 MFMA and
+//    with no integer-to-float conversion.
 //  - logits in base 2: x = S * (s_q * sm_scale * log2 e * s_k) + delta (one fused rounding).
-//  - online softmax per 64-key tile: p = 2^(x - (m - log2 448)), so P~ = e4m3(p) uses the whole
+//  - online softmax per 128-key tile: p = 2^(x - (m - log2 448)), so P~ = e4m3(p) uses the whole
 //    FP8 range; the row max is reduced within the lane and across the two half-waves.
 //  - O^T += V^T P~^T on v_mfma_scale_f32_32x32x64_f8f6f4 (fp8 x fp8, unit scales). The P~ operand
 //    is the S^T accumulator itself after conversion; V is stored in the matching key order.
 //    The fp8 MFMA's internal accumulation is not exact FP32 on gfx950 (measured error up to about
 //    2^-11 of the largest product's binade per instruction), so each tile's product is formed from
-//    zero and folded into the FP32 output registers: O = alpha*O + inner (two-level accumulation).
+//    zero, accumulated in the MFMA over the tile's two 64-key halves, and folded into the FP32
+//    output registers: O = alpha*O + inner (two-level accumulation).
 //  - epilogue: O * s_v / l, rounded to the output dtype.
 #include "device_common.h"
 
@@ -28,29 +32,6 @@ namespace sage2 {
 namespace {
 
 constexpr float kLog2_448 = 8.80735492205760410750f;
-
-// 8 packed bytes (16 INT4 codes, channel 2i in the low nibble of byte i) -> MFMA i8 operand holding
-// 16*code. Q and K use the same routine, so their slot orders agree.
-__device__ inline v4i unpack16(uint32_t w0, uint32_t w1) {
-  v4i r;
-  r[0] = (int)((w0 << 4) & 0xF0F0F0F0u);
-  r[1] = (int)(w0 & 0xF0F0F0F0u);
-  r[2] = (int)((w1 << 4) & 0xF0F0F0F0u);
-  r[3] = (int)(w1 & 0xF0F0F0F0u);
-  return r;
-}
-
-// Loads this lane-half's D/4 packed bytes of one code row and unpacks them into D/32 operands.
-template <int D>
-__device__ inline void load_codes(const uint8_t* row, int hh, v4i (&op)[D / 32]) {
-  const uint4* src = reinterpret_cast<const uint4*>(row + hh * (D / 4));
-#pragma unroll
-  for (int u = 0; u < D / 64; ++u) {
-    const uint4 w = src[u];
-    op[2 * u] = unpack16(w.x, w.y);
-    op[2 * u + 1] = unpack16(w.z, w.w);
-  }
-}
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -88,67 +69,99 @@ __device__ inline void decode_work(int L, int nqb, int Hq, int grp, int* qb, int
   *h = w % Hq;
 }
 
-// LDS staging of one 64-key tile: K as unpacked i8 operands (16*code), V in its tile layout with
-// padded channel rows, the tile's 64 correction values and its 4 K group scales.
+constexpr int kBN = 128;  // keys per tile of the online softmax
+
+// LDS staging of one 128-key tile: K as packed e2m3 code rows (8-byte padded: conflict-free 8-byte
+// reads), V as two 64-key tiles in their layout with padded channel rows, the tile's 128
+// correction values and its 8 K group scales.
 template <int D>
 struct Stage {
-  static constexpr int KROW = D + 16;          // bytes per K row (16 bytes of padding)
-  static constexpr int VCH = 80;               // bytes per V channel (64 keys + 16 padding)
+  static constexpr int CB = 3 * D / 4;                  // bytes of one packed code row
+  static constexpr int KROW = CB + 8;
+  static constexpr int VCH = 80;                        // bytes per V channel (64 keys + padding)
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = 64 * KROW;
-  static constexpr int D_OFF = V_OFF + D * VCH;
-  static constexpr int S_OFF = D_OFF + 64 * 4;
-  static constexpr int BYTES = S_OFF + 16;
-  static constexpr int K_THREADS = 64 * D / 32;  // 16 packed bytes per thread
-  static constexpr int V_BYTES = 64 * D / 256;   // per thread
+  static constexpr int V_OFF = (kBN * KROW + 15) / 16 * 16;
+  static constexpr int VHALF = D * VCH;
+  static constexpr int D_OFF = V_OFF + 2 * VHALF;
+  static constexpr int S_OFF = D_OFF + kBN * 4;
+  static constexpr int BYTES = S_OFF + 32;
+  static constexpr int K_BYTES = kBN * CB / 256;        // staged per thread
+  static constexpr int V_BYTES = 2 * 64 * D / 256;
 };
 
 template <int D>
-struct TileRegs {
-  uint4 k;
-  uint4 v[Stage<D>::V_BYTES / 16];
+struct TileK {  // K codes, correction values and group scales of one tile
+  uint2 k[Stage<D>::K_BYTES / 8];
   uint4 dl;
 };
+template <int D>
+struct TileV {  // V codes of one tile
+  uint4 v[Stage<D>::V_BYTES / 16];
+};
 
 template <int D>
-__device__ inline void tile_load(TileRegs<D>& r, int tid, int t, const uint8_t* kcode,
-                                 const uint8_t* v8, const float* drow, const float* skp) {
+__device__ inline void load_k(TileK<D>& r, int tid, int t, const uint8_t* kcode, const float* drow,
+                              const float* skp) {
   using S = Stage<D>;
-  if (tid < S::K_THREADS) {
-    const int key = tid / (D / 32), part = tid % (D / 32);
-    r.k = *reinterpret_cast<const uint4*>(kcode + (int64_t)(t * 64 + key) * (D / 2) + part * 16);
-  }
-  const uint4* vs = reinterpret_cast<const uint4*>(v8 + (int64_t)t * 64 * D + tid * S::V_BYTES);
+  const uint2* ks = reinterpret_cast<const uint2*>(kcode + (int64_t)t * kBN * S::CB + tid * S::K_BYTES);
+#pragma unroll
+  for (int u = 0; u < S::K_BYTES / 8; ++u) r.k[u] = ks[u];
+  if (tid < 32) r.dl = *reinterpret_cast<const uint4*>(drow + t * kBN + tid * 4);
+  else if (tid < 34) r.dl = *reinterpret_cast<const uint4*>(skp + 8 * t + 4 * (tid - 32));
+}
+
+template <int D>
+__device__ inline void store_k(const TileK<D>& r, int tid, uint8_t* st) {
+  using S = Stage<D>;
+  const int ko = tid * S::K_BYTES;  // K_BYTES divides CB: a thread's bytes stay in one row
+  uint2* kd = reinterpret_cast<uint2*>(st + S::K_OFF + (ko / S::CB) * S::KROW + ko % S::CB);
+#pragma unroll
+  for (int u = 0; u < S::K_BYTES / 8; ++u) kd[u] = r.k[u];
+  if (tid < 32) *reinterpret_cast<uint4*>(st + S::D_OFF + tid * 16) = r.dl;
+  else if (tid < 34) *reinterpret_cast<uint4*>(st + S::S_OFF + (tid - 32) * 16) = r.dl;
+}
+
+template <int D>
+__device__ inline void load_v(TileV<D>& r, int tid, int t, const uint8_t* v8) {
+  using S = Stage<D>;
+  const uint4* vs = reinterpret_cast<const uint4*>(v8 + (int64_t)t * kBN * D + tid * S::V_BYTES);
 #pragma unroll
   for (int u = 0; u < S::V_BYTES / 16; ++u) r.v[u] = vs[u];
-  if (tid < 16) r.dl = *reinterpret_cast<const uint4*>(drow + t * 64 + tid * 4);
-  else if (tid == 16) r.dl = *reinterpret_cast<const uint4*>(skp + 4 * t);
 }
 
 template <int D>
-__device__ inline void tile_store(const TileRegs<D>& r, int tid, uint8_t* st) {
+__device__ inline void store_v(const TileV<D>& r, int tid, uint8_t* st) {
   using S = Stage<D>;
-  if (tid < S::K_THREADS) {
-    const int key = tid / (D / 32), part = tid % (D / 32);
-    const v4i lo = unpack16(r.k.x, r.k.y), hi = unpack16(r.k.z, r.k.w);
-    uint4* dst = reinterpret_cast<uint4*>(st + S::K_OFF + key * S::KROW + part * 32);
-    dst[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    dst[1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  }
-  const int o = tid * S::V_BYTES;
-  uint4* vd = reinterpret_cast<uint4*>(st + S::V_OFF + (o / 64) * S::VCH + (o % 64));
+  const int vo = tid * S::V_BYTES;  // V_BYTES divides 64: a thread's bytes stay in one channel row
+  const int vhalf = vo / (64 * D), vr = vo % (64 * D);
+  uint4* vd = reinterpret_cast<uint4*>(st + S::V_OFF + vhalf * S::VHALF + (vr / 64) * S::VCH + vr % 64);
 #pragma unroll
   for (int u = 0; u < S::V_BYTES / 16; ++u) vd[u] = r.v[u];
-  if (tid < 16) *reinterpret_cast<uint4*>(st + S::D_OFF + tid * 16) = r.dl;
-  else if (tid == 16) *reinterpret_cast<uint4*>(st + S::S_OFF) = r.dl;
 }
 
-// One workgroup = one (sequence, q head, 128-query block); 4 waves x 32 queries. K/V tiles of 64
+// One fp6 MFMA operand: 32 e2m3 fields (24 bytes) read as three 8-byte words.
+__device__ inline v8i load_fp6_op(const uint8_t* p) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  const uint2 b = *reinterpret_cast<const uint2*>(p + 8);
+  const uint2 c = *reinterpret_cast<const uint2*>(p + 16);
+  return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+}
+
+__device__ inline v16f mfma_fp6(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, 0, 0, 0);
+}
+
+__device__ inline v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// One workgroup = one (sequence, q head, 128-query block); 4 waves x 32 queries. K/V tiles of 128
 // keys are staged once per workgroup in LDS (double-buffered, next tile's global loads in flight
 // while the current tile is computed).
 template <int D, int CAUSAL, int OUT>
 __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
-  constexpr int NCH = D / 32;
+  constexpr int NC6 = D / 64;   // fp6 MFMAs per 32-key subtile (64 channels each)
+  constexpr int NCB = D / 32;   // 32-channel blocks of the output
   using S = Stage<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BYTES];
 
@@ -165,108 +178,129 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
   const int koff = s.kv_len - s.q_len;
 
-  v4i qop[NCH];
-  load_codes<D>(ws_ptr<uint8_t>(a, a.lay.qcode) + prow * (D / 2), hh, qop);
-  // (s_q * L) * 2^-8: the 2^-8 undoes the 16*16 carried by the two operands (exact).
-  const float cq = (ws_ptr<float>(a, a.lay.sq)[prow] * a.L) * 0.00390625f;
+  v8i qop[NC6];
+  {
+    const uint8_t* qrow = ws_ptr<uint8_t>(a, a.lay.qcode) + prow * S::CB + hh * (S::CB / 2);
+#pragma unroll
+    for (int cb = 0; cb < NC6; ++cb) qop[cb] = load_fp6_op(qrow + 24 * cb);
+  }
+  const float cq = ws_ptr<float>(a, a.lay.sq)[prow] * a.L;
 
   // tiles for the workgroup (all waves stage) and for this wave (causal: up to its last row)
-  int nt = (s.kv_len + kKVTile - 1) / kKVTile;
+  int nt = (s.kv_len + kBN - 1) / kBN;
   int nt_w = nt;
   const int wave_row0 = qb * kQBlock + 32 * wave;
   if (CAUSAL) {
     const int kmax = min(s.q_len, qb * kQBlock + kQBlock) - 1 + koff;
-    nt = kmax < 0 ? 0 : min(nt, kmax / kKVTile + 1);
+    nt = kmax < 0 ? 0 : min(nt, kmax / kBN + 1);
     const int kmax_w = min(s.q_len, wave_row0 + 32) - 1 + koff;
-    nt_w = kmax_w < 0 ? 0 : min(nt_w, kmax_w / kKVTile + 1);
+    nt_w = kmax_w < 0 ? 0 : min(nt_w, kmax_w / kBN + 1);
   }
-  const uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * (D / 2);
+  const uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * S::CB;
   const float* skp = ws_ptr<float>(a, a.lay.sk) + (int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16;
   const uint8_t* v8 = ws_ptr<uint8_t>(a, a.lay.v8) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * D;
   const float* drow = ws_ptr<float>(a, a.lay.delta) + (int64_t)h * a.lay.delta_len + s.delta0 +
                       (int64_t)qb * kvpad;
 
   float m = kNegInf, lsum = 0.0f;
-  v16f o[NCH];
+  v16f o[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCH; ++cb) o[cb] = v16f{};
+  for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{};
 
-  TileRegs<D> tr;
+  TileK<D> tk;
+  TileV<D> tv;
   if (nt > 0) {
-    tile_load<D>(tr, tid, 0, kcode, v8, drow, skp);
-    tile_store<D>(tr, tid, smem);
+    load_k<D>(tk, tid, 0, kcode, drow, skp);
+    load_v<D>(tv, tid, 0, v8);
+    store_k<D>(tk, tid, smem);
+    store_v<D>(tv, tid, smem);
   }
   __syncthreads();
 
+#pragma unroll 1
   for (int t = 0; t < nt; ++t) {
     uint8_t* st = smem + (t & 1) * S::BYTES;
     const bool more = t + 1 < nt;
-    if (more) tile_load<D>(tr, tid, t + 1, kcode, v8, drow, skp);
+    uint8_t* nxt = smem + ((t + 1) & 1) * S::BYTES;  // last read before the previous barrier
+    // next tile's K part: loads issued now, written to LDS after this tile's QK^T products
+    if (more) load_k<D>(tk, tid, t + 1, kcode, drow, skp);
     if (t < nt_w) {
       // the wave needs masking only on a ragged last tile or where the causal edge crosses
-      const bool need_mask = (t * kKVTile + kKVTile > s.kv_len) ||
-                             (CAUSAL && t * kKVTile + kKVTile - 1 > wave_row0 + koff);
+      const bool need_mask = (t * kBN + kBN > s.kv_len) ||
+                             (CAUSAL && t * kBN + kBN - 1 > wave_row0 + koff);
       const float* sks = reinterpret_cast<const float*>(st + S::S_OFF);
-      float x[32];
+      float x[64];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const uint8_t* krow = st + S::K_OFF + (32 * sub + n) * S::KROW + hh * (D / 2);
-        v16i acc = v16i{};
+      for (int sub = 0; sub < 4; ++sub) {
+        const uint8_t* krow = st + S::K_OFF + (32 * sub + n) * S::KROW + hh * (S::CB / 2);
+        v16f acc = v16f{};
 #pragma unroll
-        for (int cb = 0; cb < NCH; ++cb) {
-          const v4i kop = *reinterpret_cast<const v4i*>(krow + cb * 16);
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[cb], acc, 0, 0, 0);
-        }
+        for (int cb = 0; cb < NC6; ++cb) acc = mfma_fp6(load_fp6_op(krow + 24 * cb), qop[cb], acc);
+        __builtin_amdgcn_sched_barrier(0);
         const float cs = cq * sks[2 * sub + hh];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const float4 dl = *reinterpret_cast<const float4*>(st + S::D_OFF + (32 * sub + 8 * a4 + 4 * hh) * 4);
           const float dv[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[16 * sub + 4 * a4 + e] = __builtin_fmaf((float)acc[4 * a4 + e], cs, dv[e]);
+          for (int e = 0; e < 4; ++e) x[16 * sub + 4 * a4 + e] = __builtin_fmaf(acc[4 * a4 + e], cs, dv[e]);
         }
       }
+      if (more) store_k<D>(tk, tid, nxt);
       if (need_mask) {
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          const int key = t * kKVTile + 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * hh + (k & 3);
+        for (int k = 0; k < 64; ++k) {
+          const int key = t * kBN + 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * hh + (k & 3);
           const bool vis = key < s.kv_len && (!CAUSAL || key <= i + koff);
           x[k] = vis ? x[k] : kNegInf;
         }
       }
       float mt = x[0];
 #pragma unroll
-      for (int k = 1; k < 32; ++k) mt = fmaxf(mt, x[k]);
+      for (int k = 1; k < 64; ++k) mt = fmaxf(mt, x[k]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float mnew = fmaxf(m, mt);
       const float alpha = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
       const float mb = (mnew == kNegInf) ? 0.0f : mnew - kLog2_448;
       float ps = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
+      for (int k = 0; k < 64; ++k) {
         x[k] = __builtin_amdgcn_exp2f(x[k] - mb);
         ps += x[k];
       }
       lsum = alpha * lsum + ps;
-      v8i pop;
+      v8i pop[2];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < 16; ++q) {
         const int w = cvt_fp8x2(x[4 * q], x[4 * q + 1], 0, false);
-        pop[q] = cvt_fp8x2(x[4 * q + 2], x[4 * q + 3], w, true);
+        pop[q >> 3][q & 7] = cvt_fp8x2(x[4 * q + 2], x[4 * q + 3], w, true);
       }
+      // next tile's V part: loads land during the PV products
+      if (more) load_v<D>(tv, tid, t + 1, v8);
 #pragma unroll
-      for (int cb = 0; cb < NCH; ++cb) {
-        const uint8_t* vrow = st + S::V_OFF + (32 * cb + n) * S::VCH + hh * 32;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(vrow);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + 16);
-        const v8i vop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        const v16f inner = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, v16f{}, 0, 0, 0, 0, 0, 0);
+      for (int cb = 0; cb < NCB; ++cb) {
+        v16f inner = v16f{};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint8_t* vrow = st + S::V_OFF + half * S::VHALF + (32 * cb + n) * S::VCH + hh * 32;
+          const uint4 v0 = *reinterpret_cast<const uint4*>(vrow);
+          const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + 16);
+          const v8i vop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+          inner = mfma_fp8(vop, pop[half], inner);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(alpha, o[cb][r], inner[r]);
+        // one channel block at a time: keeps the V operands and partial products of the other
+        // blocks out of registers
+        __builtin_amdgcn_sched_barrier(0);
       }
       m = mnew;
+      if (more) store_v<D>(tv, tid, nxt);
+    } else if (more) {
+      store_k<D>(tk, tid, nxt);
+      load_v<D>(tv, tid, t + 1, v8);
+      store_v<D>(tv, tid, nxt);
     }
-    if (more) tile_store<D>(tr, tid, smem + ((t + 1) & 1) * S::BYTES);
     __syncthreads();
   }
 
@@ -277,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   constexpr int ES = OUT == SAGE2_F32 ? 4 : 2;
   char* orow = reinterpret_cast<char*>(a.o) + ES * row_index(a.os, b, s.q_start + i, h);
 #pragma unroll
-  for (int cb = 0; cb < NCH; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int c0 = 32 * cb + 8 * a4 + 4 * hh;
@@ -288,10 +322,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   }
 }
 
-// Test-only: the same INT4 MFMA path, dumping S = acc / 256 for rows [dbg_q0, dbg_q0 + dbg_qn).
+// Test-only: the same fp6 MFMA path, dumping S for rows [dbg_q0, dbg_q0 + dbg_qn).
 template <int D>
 __global__ __launch_bounds__(256) void k_debug_qk(KArgs a) {
-  constexpr int NCH = D / 32;
+  constexpr int NC6 = D / 64;
+  constexpr int CB = 3 * D / 4;
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
   if (qb * kQBlock + kQBlock <= a.dbg_q0 || qb * kQBlock >= a.dbg_q0 + a.dbg_qn) return;
@@ -301,32 +336,29 @@ __global__ __launch_bounds__(256) void k_debug_qk(KArgs a) {
   const int i = qb * kQBlock + 32 * wave + n;
   const bool row_out = i >= a.dbg_q0 && i < a.dbg_q0 + a.dbg_qn;
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
-  v4i qop[NCH];
+  v8i qop[NC6];
+#pragma unroll
+  for (int cb = 0; cb < NC6; ++cb) qop[cb] = v8i{};
   if (blk_ok) {
-    load_codes<D>(ws_ptr<uint8_t>(a, a.lay.qcode) + ((int64_t)h * a.lay.q_rows + s.q_row0 + i) * (D / 2), hh, qop);
-  } else {
+    const uint8_t* qrow = ws_ptr<uint8_t>(a, a.lay.qcode) + ((int64_t)h * a.lay.q_rows + s.q_row0 + i) * CB + hh * (CB / 2);
 #pragma unroll
-    for (int cb = 0; cb < NCH; ++cb) qop[cb] = v4i{};
+    for (int cb = 0; cb < NC6; ++cb) qop[cb] = load_fp6_op(qrow + 24 * cb);
   }
-  const uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * (D / 2);
+  const uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * CB;
   int32_t* out = a.dbg_out + (((int64_t)b * a.Hq + h) * a.dbg_qn + (i - a.dbg_q0)) * a.Nkv;
-  const int nt = (a.Nkv + kKVTile - 1) / kKVTile;
-  for (int t = 0; t < nt; ++t) {
+  const int nsub = (a.Nkv + 31) / 32;
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int key0 = 32 * sub;
+    v16f acc = v16f{};
+    if (blk_ok && key0 < kvpad) {
+      const uint8_t* krow = kcode + (int64_t)(key0 + n) * CB + hh * (CB / 2);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int key0 = t * kKVTile + 32 * st;
-      v16i acc = v16i{};
-      if (blk_ok && key0 < kvpad) {
-        v4i kop[NCH];
-        load_codes<D>(kcode + (int64_t)(key0 + n) * (D / 2), hh, kop);
+      for (int cb = 0; cb < NC6; ++cb) acc = mfma_fp6(load_fp6_op(krow + 24 * cb), qop[cb], acc);
+    }
 #pragma unroll
-        for (int cb = 0; cb < NCH; ++cb) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[cb], qop[cb], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (row_out && key < a.Nkv) out[key] = (i < s.q_len && key < s.kv_len) ? (acc[r] >> 8) : 0;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (row_out && key < a.Nkv) out[key] = (i < s.q_len && key < s.kv_len) ? (int32_t)acc[r] : 0;
     }
   }
 }

@@ -94,9 +94,9 @@ void compute_layout(const sage2_params* p, sage2_ws_layout* L) {
   L->sv = take((int64_t)p->B * p->H_kv * d * 4);
   L->sv_inv = take((int64_t)p->B * p->H_kv * d * 4);
   L->qbar = take(p->H_q * L->q_blocks * d * 4);
-  L->qcode = take(p->H_q * L->q_rows * d / 2);
+  L->qcode = take(p->H_q * L->q_rows * d * 3 / 4);
   L->sq = take(p->H_q * L->q_rows * 4);
-  L->kcode = take(p->H_kv * L->kv_rows * d / 2);
+  L->kcode = take(p->H_kv * L->kv_rows * d * 3 / 4);
   L->sk = take(p->H_kv * (L->kv_rows / 16) * 4);
   L->v8 = take(p->H_kv * L->kv_rows * d);
   L->delta = take(p->H_q * L->delta_len * 4);

@@ -103,16 +103,35 @@ __device__ inline int int4_code(float x, float inv) {
   return (int)fminf(7.0f, fmaxf(-7.0f, rintf(y)));
 }
 
-// Packs this lane's codes (C = D/64 consecutive channels per lane) into the row's bytes: byte i
-// holds channel 2i in its low nibble and channel 2i+1 in its high nibble.
-template <int C>
-__device__ inline void store_codes(uint8_t* row, const int (&code)[C], int lane) {
-  if constexpr (C == 2) {
-    row[lane] = (uint8_t)((code[0] & 0xF) | ((code[1] & 0xF) << 4));
-  } else {
-    const int nb = __shfl_down(code[0], 1, 64);
-    if ((lane & 1) == 0) row[lane >> 1] = (uint8_t)((code[0] & 0xF) | ((nb & 0xF) << 4));
+// e2m3 (FP6) encoding of an INT4 code: every integer in [-7, 7] is exact in e2m3 (1 sign,
+// 2 exponent, 3 mantissa bits; magnitudes 1 2 3 4 5 6 7 = 001000 010000 010100 011000 011010
+// 011100 011110). The attention kernel feeds these fields to the fp6 MFMA, whose f32 accumulation
+// of such small integer products is exact.
+__device__ inline uint32_t e2m3_of_int4(int c) {
+  const int m = c < 0 ? -c : c;
+  const uint32_t mag = (uint32_t)(0x1E1C1A1814100800ull >> (8 * m)) & 0x3Fu;
+  return mag | (c < 0 ? 0x20u : 0u);
+}
+
+// Writes one row of D INT4 codes (C = D/64 consecutive channels per lane) as packed e2m3 fields:
+// channel ch occupies bits [6 ch, 6 ch + 6) of the row, little-endian across dwords (3D/16 dwords).
+// buf: this wave's D-byte LDS scratch. Every thread of the block must call it (it synchronizes).
+template <int D, int C>
+__device__ inline void store_row_fp6(uint32_t* row, const int (&code)[C], int lane, uint8_t* buf) {
+#pragma unroll
+  for (int e = 0; e < C; ++e) buf[lane * C + e] = (uint8_t)e2m3_of_int4(code[e]);
+  __syncthreads();
+  if (lane < 3 * D / 16) {
+    const int c0 = (32 * lane) / 6, c1 = (32 * lane + 31) / 6;
+    uint32_t w = 0;
+    for (int ch = c0; ch <= c1; ++ch) {
+      const int sh = 6 * ch - 32 * lane;
+      const uint32_t v = buf[ch];
+      w |= sh >= 0 ? (v << sh) : (v >> -sh);
+    }
+    row[lane] = w;
   }
+  __syncthreads();
 }
 
 // ---- Q: block mean, per-token INT4 codes -------------------------------------------------------
@@ -128,6 +147,7 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
   if (qb * kQBlock >= s.q_len) return;
   const int i0 = qb * kQBlock, n = min(kQBlock, s.q_len - i0);
   __shared__ float qbar[D];
+  __shared__ uint8_t cbuf[4][D];
   if (tid < D) {
     double sum = 0.0;
     for (int i = 0; i < n; ++i) sum += (double)ld_in<IN>(a.q, row_index(a.qs, b, s.q_start + i0 + i, h) + tid);
@@ -161,7 +181,7 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
 #pragma unroll
       for (int e = 0; e < C; ++e) code[e] = 0;
     }
-    store_codes<C>(qcode + prow * (D / 2), code, lane);
+    store_row_fp6<D, C>(reinterpret_cast<uint32_t*>(qcode + prow * (3 * D / 4)), code, lane, cbuf[wave]);
     if (lane == 0) sq[prow] = scale;
   }
 }
@@ -183,6 +203,7 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
   if (t * kKVTile >= kvpad) return;
   __shared__ float kbar[D], svinv[D];
   __shared__ float vt[kKVTile][D + 1];
+  __shared__ uint8_t cbuf[4][D];
   const int64_t sidx = ((int64_t)b * a.Hkv + g) * D;
   if (tid < D) {
     kbar[tid] = ws_ptr<float>(a, a.lay.kbar)[sidx + tid];
@@ -216,7 +237,8 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
       int code[C];
 #pragma unroll
       for (int x = 0; x < C; ++x) code[x] = int4_code(kt[e][x], inv);
-      store_codes<C>(kcode + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (D / 2), code, lane);
+      store_row_fp6<D, C>(reinterpret_cast<uint32_t*>(kcode + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (3 * D / 4)),
+                          code, lane, cbuf[wave]);
     }
     if (lane == 0)
       ws_ptr<float>(a, a.lay.sk)[(int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16 + 4 * t + wave] = scale;

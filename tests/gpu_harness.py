@@ -81,13 +81,17 @@ class GpuRun:
             nbytes = count * np.dtype(dtype).itemsize
             return ws[off:off + nbytes].view(dtype)
 
-        def unpack(raw):  # [..., d/2] u8 -> [..., d] int8
-            lo = (raw & 0xF).astype(np.int8)
-            hi = (raw >> 4).astype(np.int8)
-            lo = np.where(lo >= 8, lo - 16, lo).astype(np.int8)
-            hi = np.where(hi >= 8, hi - 16, hi).astype(np.int8)
-            out = np.empty(raw.shape[:-1] + (raw.shape[-1] * 2,), np.int8)
-            out[..., 0::2], out[..., 1::2] = lo, hi
+        def unpack(raw):  # [..., 3d/4] u8 of packed e2m3 fields -> [..., d] int8 codes
+            bits = np.unpackbits(raw, axis=-1, bitorder="little")
+            f = bits.reshape(raw.shape[:-1] + (raw.shape[-1] * 8 // 6, 6))
+            v = (f * (1 << np.arange(6))).sum(-1)
+            table = {0: 0, 8: 1, 16: 2, 20: 3, 24: 4, 26: 5, 28: 6, 30: 7}
+            mag = np.full(v.shape, 99, np.int8)
+            for k_, m_ in table.items():
+                mag[(v & 31) == k_] = m_
+            assert not (mag == 99).any(), "field that is not an INT4 code in e2m3"
+            out = np.where(v & 32, -mag, mag).astype(np.int8)
+            assert not ((v == 32).any()), "negative zero code"
             return out
 
         out = {"table": (qs, lq, ks, lk, qrow0, kvrow0, qblk0, delta0)}
@@ -95,12 +99,12 @@ class GpuRun:
         out["sv"] = arr(lay.sv, np.float32, self.p.B * Hkv * d).reshape(self.p.B, Hkv, d)[b]
         qbar = arr(lay.qbar, np.float32, Hq * lay.q_blocks * d).reshape(Hq, lay.q_blocks, d)
         out["qbar"] = qbar[:, qblk0:qblk0 + nqb]
-        qc = arr(lay.qcode, np.uint8, Hq * lay.q_rows * d // 2).reshape(Hq, lay.q_rows, d // 2)
+        qc = arr(lay.qcode, np.uint8, Hq * lay.q_rows * 3 * d // 4).reshape(Hq, lay.q_rows, 3 * d // 4)
         out["qcode"] = unpack(qc[:, qrow0:qrow0 + lq])
         out["qcode_pad"] = unpack(qc[:, qrow0 + lq:qrow0 + nqb * 128])
         sq = arr(lay.sq, np.float32, Hq * lay.q_rows).reshape(Hq, lay.q_rows)
         out["sq"] = sq[:, qrow0:qrow0 + lq]
-        kc = arr(lay.kcode, np.uint8, Hkv * lay.kv_rows * d // 2).reshape(Hkv, lay.kv_rows, d // 2)
+        kc = arr(lay.kcode, np.uint8, Hkv * lay.kv_rows * 3 * d // 4).reshape(Hkv, lay.kv_rows, 3 * d // 4)
         out["kcode"] = unpack(kc[:, kvrow0:kvrow0 + lk])
         sk = arr(lay.sk, np.float32, Hkv * lay.kv_rows // 16).reshape(Hkv, lay.kv_rows // 16)
         out["sk"] = sk[:, kvrow0 // 16:kvrow0 // 16 + 2 * ((lk + 31) // 32)]
