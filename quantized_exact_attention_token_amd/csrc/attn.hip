@@ -71,73 +71,96 @@ __device__ inline void decode_work(int L, int nqb, int Hq, int grp, int* qb, int
 
 constexpr int kBN = 128;  // keys per tile of the online softmax
 
-// LDS staging of one 128-key tile: K as packed e2m3 code rows (8-byte padded: conflict-free 8-byte
-// reads), V as two 64-key tiles in their layout with padded channel rows, the tile's 128
-// correction values and its 8 K group scales.
+// LDS staging of one 128-key tile, filled by global->LDS DMA (global_load_lds_dwordx4: lane i of
+// an instruction writes 16 bytes at base + 16 i, from any global address). Each region is a
+// permutation of 16-byte blocks chosen so that the compute reads hit distinct banks:
+//  - K: 128 packed e2m3 rows of R = 3D/64 blocks. For D = 128 the two 3-block halves of a row swap
+//    places every 8 keys (block j of key k at 6k + ((j + 3*((k>>3)&1)) mod 6)), so 16 lanes reading
+//    one block each of 16 consecutive keys land on 16 different 16-byte bank groups; for D = 64
+//    rows of 3 blocks already do.
+//  - V: two 64-key tiles, D channels x 4 blocks (the layout of the workspace's v8 tiles), block j
+//    of channel c at 4c + (j ^ ((c>>2)&3)).
+//  - the tile's 128 correction values and its 8 K group scales, contiguous.
 template <int D>
 struct Stage {
-  static constexpr int CB = 3 * D / 4;                  // bytes of one packed code row
-  static constexpr int KROW = CB + 8;
-  static constexpr int VCH = 80;                        // bytes per V channel (64 keys + padding)
+  static constexpr int CB = 3 * D / 4;         // bytes of one packed code row
+  static constexpr int R = CB / 16;            // 16-byte blocks per code row
+  static constexpr int KB = kBN * R;           // K blocks
+  static constexpr int VB = 2 * D * 4;         // V blocks
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = (kBN * KROW + 15) / 16 * 16;
-  static constexpr int VHALF = D * VCH;
-  static constexpr int D_OFF = V_OFF + 2 * VHALF;
+  static constexpr int V_OFF = KB * 16;
+  static constexpr int D_OFF = V_OFF + VB * 16;
   static constexpr int S_OFF = D_OFF + kBN * 4;
   static constexpr int BYTES = S_OFF + 32;
-  static constexpr int K_BYTES = kBN * CB / 256;        // staged per thread
-  static constexpr int V_BYTES = 2 * 64 * D / 256;
+  static constexpr int K_INSTR = KB / 64;      // DMA instructions per region (64 blocks each)
+  static constexpr int V_INSTR = VB / 64;
+};
+
+// LDS block of K (key k, row block j)
+template <int D>
+__device__ inline int k_block(int k, int j) {
+  if constexpr (Stage<D>::R == 6) return 6 * k + (j + 3 * ((k >> 3) & 1)) % 6;
+  else return Stage<D>::R * k + j;
+}
+// LDS block of V (64-key half h2, channel c, block j)
+template <int D>
+__device__ inline int v_block(int h2, int c, int j) {
+  return h2 * (4 * D) + 4 * c + (j ^ ((c >> 2) & 3));
+}
+
+// Per-lane byte offsets (relative to a tile's global base) of the blocks this lane fetches.
+template <int D>
+struct DmaPlan {
+  int k[(Stage<D>::K_INSTR + 3) / 4];
+  int v[(Stage<D>::V_INSTR + 3) / 4];
 };
 
 template <int D>
-struct TileK {  // K codes, correction values and group scales of one tile
-  uint2 k[Stage<D>::K_BYTES / 8];
-  uint4 dl;
-};
-template <int D>
-struct TileV {  // V codes of one tile
-  uint4 v[Stage<D>::V_BYTES / 16];
-};
-
-template <int D>
-__device__ inline void load_k(TileK<D>& r, int tid, int t, const uint8_t* kcode, const float* drow,
-                              const float* skp) {
+__device__ inline DmaPlan<D> make_dma_plan(int wave, int lane) {
   using S = Stage<D>;
-  const uint2* ks = reinterpret_cast<const uint2*>(kcode + (int64_t)t * kBN * S::CB + tid * S::K_BYTES);
+  DmaPlan<D> pl;
 #pragma unroll
-  for (int u = 0; u < S::K_BYTES / 8; ++u) r.k[u] = ks[u];
-  if (tid < 32) r.dl = *reinterpret_cast<const uint4*>(drow + t * kBN + tid * 4);
-  else if (tid < 34) r.dl = *reinterpret_cast<const uint4*>(skp + 8 * t + 4 * (tid - 32));
+  for (int u = 0; u < (S::K_INSTR + 3) / 4; ++u) {
+    const int p = (wave + 4 * u) * 64 + lane;   // LDS block written by this lane
+    int k = p / S::R, jj = p % S::R, j = jj;
+    if constexpr (S::R == 6) j = (jj + 6 - 3 * ((k >> 3) & 1)) % 6;
+    pl.k[u] = k * S::CB + 16 * j;
+  }
+#pragma unroll
+  for (int u = 0; u < (S::V_INSTR + 3) / 4; ++u) {
+    const int p = (wave + 4 * u) * 64 + lane;
+    const int h2 = p / (4 * D), r = p % (4 * D), c = r / 4, j = (r % 4) ^ ((c >> 2) & 3);
+    pl.v[u] = h2 * (64 * D) + c * 64 + 16 * j;
+  }
+  return pl;
 }
 
-template <int D>
-__device__ inline void store_k(const TileK<D>& r, int tid, uint8_t* st) {
-  using S = Stage<D>;
-  const int ko = tid * S::K_BYTES;  // K_BYTES divides CB: a thread's bytes stay in one row
-  uint2* kd = reinterpret_cast<uint2*>(st + S::K_OFF + (ko / S::CB) * S::KROW + ko % S::CB);
-#pragma unroll
-  for (int u = 0; u < S::K_BYTES / 8; ++u) kd[u] = r.k[u];
-  if (tid < 32) *reinterpret_cast<uint4*>(st + S::D_OFF + tid * 16) = r.dl;
-  else if (tid < 34) *reinterpret_cast<uint4*>(st + S::S_OFF + (tid - 32) * 16) = r.dl;
+__device__ inline void dma16(const void* src, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
+// Issues the DMA of tile t into stage `st` (every wave its share).
 template <int D>
-__device__ inline void load_v(TileV<D>& r, int tid, int t, const uint8_t* v8) {
+__device__ inline void issue_tile(const DmaPlan<D>& pl, int wave, int lane, int t, uint8_t* st,
+                                  const uint8_t* kcode, const uint8_t* v8, const float* drow,
+                                  const float* skp) {
   using S = Stage<D>;
-  const uint4* vs = reinterpret_cast<const uint4*>(v8 + (int64_t)t * kBN * D + tid * S::V_BYTES);
+  const uint8_t* kt = kcode + (int64_t)t * kBN * S::CB;
+  const uint8_t* vt = v8 + (int64_t)t * kBN * D;
 #pragma unroll
-  for (int u = 0; u < S::V_BYTES / 16; ++u) r.v[u] = vs[u];
+  for (int u = 0; u < (S::K_INSTR + 3) / 4; ++u)
+    if (wave + 4 * u < S::K_INSTR) dma16(kt + pl.k[u], st + S::K_OFF + (wave + 4 * u) * 1024);
+#pragma unroll
+  for (int u = 0; u < (S::V_INSTR + 3) / 4; ++u)
+    if (wave + 4 * u < S::V_INSTR) dma16(vt + pl.v[u], st + S::V_OFF + (wave + 4 * u) * 1024);
+  if (wave == 0 && lane < 34) {
+    const void* src = lane < 32 ? (const void*)(drow + t * kBN + 4 * lane)
+                                : (const void*)(skp + 8 * t + 4 * (lane - 32));
+    dma16(src, st + S::D_OFF);
+  }
 }
 
-template <int D>
-__device__ inline void store_v(const TileV<D>& r, int tid, uint8_t* st) {
-  using S = Stage<D>;
-  const int vo = tid * S::V_BYTES;  // V_BYTES divides 64: a thread's bytes stay in one channel row
-  const int vhalf = vo / (64 * D), vr = vo % (64 * D);
-  uint4* vd = reinterpret_cast<uint4*>(st + S::V_OFF + vhalf * S::VHALF + (vr / 64) * S::VCH + vr % 64);
-#pragma unroll
-  for (int u = 0; u < S::V_BYTES / 16; ++u) vd[u] = r.v[u];
-}
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One fp6 MFMA operand: 32 e2m3 fields (24 bytes) read as three 8-byte words.
 __device__ inline v8i load_fp6_op(const uint8_t* p) {
@@ -207,23 +230,29 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{};
 
-  TileK<D> tk;
-  TileV<D> tv;
-  if (nt > 0) {
-    load_k<D>(tk, tid, 0, kcode, drow, skp);
-    load_v<D>(tv, tid, 0, v8);
-    store_k<D>(tk, tid, smem);
-    store_v<D>(tv, tid, smem);
-  }
+  const DmaPlan<D> plan = make_dma_plan<D>(wave, lane);
+  // per-lane LDS byte offsets of the compute reads (loop invariant)
+  int kofs[4];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) kofs[sub] = S::K_OFF + 16 * k_block<D>(32 * sub + n, S::R / 2 * hh);
+  int vofs[NCB][2][2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) vofs[cb][h2][u] = S::V_OFF + 16 * v_block<D>(h2, 32 * cb + n, 2 * hh + u);
+
+  if (nt > 0) issue_tile<D>(plan, wave, lane, 0, smem, kcode, v8, drow, skp);
+  wait_dma();
   __syncthreads();
 
 #pragma unroll 1
   for (int t = 0; t < nt; ++t) {
     uint8_t* st = smem + (t & 1) * S::BYTES;
-    const bool more = t + 1 < nt;
-    uint8_t* nxt = smem + ((t + 1) & 1) * S::BYTES;  // last read before the previous barrier
-    // next tile's K part: loads issued now, written to LDS after this tile's QK^T products
-    if (more) load_k<D>(tk, tid, t + 1, kcode, drow, skp);
+    // next tile: DMA into the other stage (last read before the previous barrier); it has this
+    // whole iteration to land
+    if (t + 1 < nt) issue_tile<D>(plan, wave, lane, t + 1, smem + ((t + 1) & 1) * S::BYTES, kcode, v8, drow, skp);
     if (t < nt_w) {
       // the wave needs masking only on a ragged last tile or where the causal edge crosses
       const bool need_mask = (t * kBN + kBN > s.kv_len) ||
@@ -232,10 +261,21 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
       float x[64];
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
-        const uint8_t* krow = st + S::K_OFF + (32 * sub + n) * S::KROW + hh * (S::CB / 2);
         v16f acc = v16f{};
-#pragma unroll
-        for (int cb = 0; cb < NC6; ++cb) acc = mfma_fp6(load_fp6_op(krow + 24 * cb), qop[cb], acc);
+        if constexpr (D == 128) {
+          // this lane's 48 bytes of the key row (rows keep their 3-block halves contiguous)
+          const uint4 b0 = *reinterpret_cast<const uint4*>(st + kofs[sub]);
+          const uint4 b1 = *reinterpret_cast<const uint4*>(st + kofs[sub] + 16);
+          const uint4 b2 = *reinterpret_cast<const uint4*>(st + kofs[sub] + 32);
+          const v8i k0 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, 0, 0};
+          const v8i k1 = {(int)b1.z, (int)b1.w, (int)b2.x, (int)b2.y, (int)b2.z, (int)b2.w, 0, 0};
+          acc = mfma_fp6(k0, qop[0], acc);
+          acc = mfma_fp6(k1, qop[NC6 - 1], acc);
+        } else {
+          // D = 64: 24 bytes at byte 24*hh of a 48-byte row
+          const uint8_t* kr = st + S::K_OFF + (32 * sub + n) * S::CB + 24 * hh;
+          acc = mfma_fp6(load_fp6_op(kr), qop[0], acc);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const float cs = cq * sks[2 * sub + hh];
 #pragma unroll
@@ -246,7 +286,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
           for (int e = 0; e < 4; ++e) x[16 * sub + 4 * a4 + e] = __builtin_fmaf(acc[4 * a4 + e], cs, dv[e]);
         }
       }
-      if (more) store_k<D>(tk, tid, nxt);
       if (need_mask) {
 #pragma unroll
         for (int k = 0; k < 64; ++k) {
@@ -275,18 +314,15 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
         const int w = cvt_fp8x2(x[4 * q], x[4 * q + 1], 0, false);
         pop[q >> 3][q & 7] = cvt_fp8x2(x[4 * q + 2], x[4 * q + 3], w, true);
       }
-      // next tile's V part: loads land during the PV products
-      if (more) load_v<D>(tv, tid, t + 1, v8);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         v16f inner = v16f{};
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint8_t* vrow = st + S::V_OFF + half * S::VHALF + (32 * cb + n) * S::VCH + hh * 32;
-          const uint4 v0 = *reinterpret_cast<const uint4*>(vrow);
-          const uint4 v1 = *reinterpret_cast<const uint4*>(vrow + 16);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint4 v0 = *reinterpret_cast<const uint4*>(st + vofs[cb][h2][0]);
+          const uint4 v1 = *reinterpret_cast<const uint4*>(st + vofs[cb][h2][1]);
           const v8i vop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-          inner = mfma_fp8(vop, pop[half], inner);
+          inner = mfma_fp8(vop, pop[h2], inner);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(alpha, o[cb][r], inner[r]);
@@ -295,12 +331,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       m = mnew;
-      if (more) store_v<D>(tv, tid, nxt);
-    } else if (more) {
-      store_k<D>(tk, tid, nxt);
-      load_v<D>(tv, tid, t + 1, v8);
-      store_v<D>(tv, tid, nxt);
     }
+    wait_dma();
     __syncthreads();
   }
 
