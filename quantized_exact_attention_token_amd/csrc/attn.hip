@@ -276,7 +276,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
           const uint8_t* kr = st + S::K_OFF + (32 * sub + n) * S::CB + 24 * hh;
           acc = mfma_fp6(load_fp6_op(kr), qop[0], acc);
         }
-        __builtin_amdgcn_sched_barrier(0);
         const float cs = cq * sks[2 * sub + hh];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
@@ -326,9 +325,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(alpha, o[cb][r], inner[r]);
-        // one channel block at a time: keeps the V operands and partial products of the other
-        // blocks out of registers
-        __builtin_amdgcn_sched_barrier(0);
       }
       m = mnew;
     }
