@@ -113,76 +113,107 @@ __device__ inline uint32_t e2m3_of_int4(int c) {
   return mag | (c < 0 ? 0x20u : 0u);
 }
 
-// Writes one row of D INT4 codes (C = D/64 consecutive channels per lane) as packed e2m3 fields:
-// channel ch occupies bits [6 ch, 6 ch + 6) of the row, little-endian across dwords (3D/16 dwords).
-// buf: this wave's D-byte LDS scratch. Every thread of the block must call it (it synchronizes).
-template <int D, int C>
-__device__ inline void store_row_fp6(uint32_t* row, const int (&code)[C], int lane, uint8_t* buf) {
+// Writes one row of D INT4 codes as packed e2m3 fields: channel ch occupies bits [6 ch, 6 ch + 6)
+// of the row, little-endian across dwords (3D/16 dwords).
+// Row-parallel form: 16 lanes per row, lane li holding channels [CPL*li, CPL*li + CPL) (CPL =
+// D/16). Leaders of groups of GL = 96/(6 CPL) lanes assemble their group's 96 bits from the
+// neighbours' fields and write them as three dwords: no block barrier.
+template <int D>
+__device__ inline void store_row_fp6_16(uint32_t* row, const int (&code)[D / 16], int li) {
+  constexpr int CPL = D / 16;
+  uint64_t v = 0;
 #pragma unroll
-  for (int e = 0; e < C; ++e) buf[lane * C + e] = (uint8_t)e2m3_of_int4(code[e]);
-  __syncthreads();
-  if (lane < 3 * D / 16) {
-    const int c0 = (32 * lane) / 6, c1 = (32 * lane + 31) / 6;
-    uint32_t w = 0;
-    for (int ch = c0; ch <= c1; ++ch) {
-      const int sh = 6 * ch - 32 * lane;
-      const uint32_t v = buf[ch];
-      w |= sh >= 0 ? (v << sh) : (v >> -sh);
+  for (int e = 0; e < CPL; ++e) v |= (uint64_t)e2m3_of_int4(code[e]) << (6 * e);
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  if constexpr (CPL == 8) {  // 48 bits per lane, pairs of lanes make 3 dwords
+    const uint32_t nlo = __shfl_down(lo, 1, 16), nhi = __shfl_down(hi, 1, 16);
+    if ((li & 1) == 0) {
+      uint32_t* dst = row + 3 * (li >> 1);
+      dst[0] = lo;
+      dst[1] = (hi & 0xFFFFu) | (nlo << 16);
+      dst[2] = (nlo >> 16) | (nhi << 16);
     }
-    row[lane] = w;
+  } else {  // CPL == 4: 24 bits per lane, quads of lanes make 3 dwords
+    const uint32_t b = __shfl_down(lo, 1, 16), c = __shfl_down(lo, 2, 16), d = __shfl_down(lo, 3, 16);
+    if ((li & 3) == 0) {
+      uint32_t* dst = row + 3 * (li >> 2);
+      dst[0] = lo | (b << 24);
+      dst[1] = (b >> 8) | (c << 16);
+      dst[2] = (c >> 16) | (d << 8);
+    }
   }
-  __syncthreads();
+}
+
+__device__ inline float max16(float x) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 16));
+  return x;
 }
 
 // ---- Q: block mean, per-token INT4 codes -------------------------------------------------------
-// grid (Q blocks, H_q, B), block 256. The block's mean is an fp64 sum over its valid rows in row
-// order; each of the 4 waves then quantizes every 4th row (one scale per token: on gfx950 a lane
-// owns one query column of the S^T = K Q^T MFMA tile, so the per-thread group is one token).
+// grid (Q blocks, H_q, B), block 256. The block's rows are read once, coalesced, into LDS; the mean
+// is an fp64 sum over the valid rows in row order (thread c: channel c); each of the 4 waves then
+// quantizes every 4th row (one scale per token: on gfx950 a lane owns one query column of the
+// S^T = K Q^T MFMA tile, so the per-thread group is one token).
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
-  constexpr int C = D / 64;
+  constexpr int RW = D / 8;  // 16-byte chunks per row
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seq s = load_seq(a, b);
   if (qb * kQBlock >= s.q_len) return;
   const int i0 = qb * kQBlock, n = min(kQBlock, s.q_len - i0);
+  __shared__ __attribute__((aligned(16))) uint16_t rows[kQBlock][D];
   __shared__ float qbar[D];
-  __shared__ uint8_t cbuf[4][D];
+  for (int idx = tid; idx < n * RW; idx += 256) {
+    const int r = idx / RW, ch = idx % RW;
+    const uint4 v = *reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(a.q) + row_index(a.qs, b, s.q_start + i0 + r, h) + 8 * ch);
+    *reinterpret_cast<uint4*>(&rows[r][8 * ch]) = v;
+  }
+  __syncthreads();
+  auto widen = [](uint16_t raw) {
+    if constexpr (IN == SAGE2_BF16) {
+      return __uint_as_float((uint32_t)raw << 16);
+    } else {
+      _Float16 hv;
+      __builtin_memcpy(&hv, &raw, 2);
+      return (float)hv;
+    }
+  };
   if (tid < D) {
     double sum = 0.0;
-    for (int i = 0; i < n; ++i) sum += (double)ld_in<IN>(a.q, row_index(a.qs, b, s.q_start + i0 + i, h) + tid);
+    for (int i = 0; i < n; ++i) sum += (double)widen(rows[i][tid]);
     const float m = (float)(sum / (double)n);
     qbar[tid] = m;
-    ws_ptr<float>(a, a.lay.qbar)[((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + tid] = m;
+    const int64_t at = ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + tid;
+    ws_ptr<float>(a, a.lay.qbar)[at] = m;
+    ws_ptr<double>(a, a.lay.qbar64)[at] = (double)m;
   }
   __syncthreads();
   uint8_t* qcode = ws_ptr<uint8_t>(a, a.lay.qcode);
   float* sq = ws_ptr<float>(a, a.lay.sq);
-  for (int r = wave; r < kQBlock; r += 4) {
+  constexpr int CPL = D / 16;
+  const int li = lane & 15;
+  for (int it = 0; it < 8; ++it) {
+    const int r = 32 * wave + 4 * it + (lane >> 4);  // 4 rows per wave at a time, 16 lanes each
     const int64_t prow = (int64_t)h * a.lay.q_rows + s.q_row0 + i0 + r;
-    int code[C];
-    float scale = 0.0f;
-    if (r < n) {
-      const int64_t base = row_index(a.qs, b, s.q_start + i0 + r, h);
-      float qt[C];
-      float amax = 0.0f;
+    int code[CPL];
+    float qt[CPL];
+    float amax = 0.0f;
 #pragma unroll
-      for (int e = 0; e < C; ++e) {
-        const int c = lane * C + e;
-        qt[e] = ld_in<IN>(a.q, base + c) - qbar[c];
-        amax = fmaxf(amax, fabsf(qt[e]));
-      }
-      amax = wave_max(amax);
-      const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
-      scale = amax == 0.0f ? 0.0f : amax / 7.0f;
-#pragma unroll
-      for (int e = 0; e < C; ++e) code[e] = int4_code(qt[e], inv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < C; ++e) code[e] = 0;
+    for (int e = 0; e < CPL; ++e) {
+      const int c = CPL * li + e;
+      qt[e] = r < n ? widen(rows[r][c]) - qbar[c] : 0.0f;
+      amax = fmaxf(amax, fabsf(qt[e]));
     }
-    store_row_fp6<D, C>(reinterpret_cast<uint32_t*>(qcode + prow * (3 * D / 4)), code, lane, cbuf[wave]);
-    if (lane == 0) sq[prow] = scale;
+    amax = max16(amax);
+    const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
+    const float scale = amax == 0.0f ? 0.0f : amax / 7.0f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) code[e] = int4_code(qt[e], inv);
+    store_row_fp6_16<D>(reinterpret_cast<uint32_t*>(qcode + prow * (3 * D / 4)), code, li);
+    if (li == 0) sq[prow] = scale;
   }
 }
 
@@ -203,7 +234,6 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
   if (t * kKVTile >= kvpad) return;
   __shared__ float kbar[D], svinv[D];
   __shared__ float vt[kKVTile][D + 1];
-  __shared__ uint8_t cbuf[4][D];
   const int64_t sidx = ((int64_t)b * a.Hkv + g) * D;
   if (tid < D) {
     kbar[tid] = ws_ptr<float>(a, a.lay.kbar)[sidx + tid];
@@ -213,7 +243,6 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
   // K group of this wave
   {
     const int half = wave & 1, sub = wave >> 1;
-    float kt[16][C];
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -223,7 +252,6 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
         const int c = lane * C + x;
         float val = 0.0f;
         if (j < s.kv_len) val = ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c];
-        kt[e][x] = val;
         amax = fmaxf(amax, fabsf(val));
       }
     }
@@ -231,14 +259,22 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
     const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
     const float scale = amax == 0.0f ? 0.0f : amax / 7.0f;
     uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode);
+    // codes: 4 keys of the group at a time, 16 lanes per key (values re-read through L1)
+    constexpr int CPL = D / 16;
+    const int li = lane & 15;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int it = 0; it < 4; ++it) {
+      const int e = 4 * it + (lane >> 4);
       const int j = t * kKVTile + 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);
-      int code[C];
+      int code[CPL];
 #pragma unroll
-      for (int x = 0; x < C; ++x) code[x] = int4_code(kt[e][x], inv);
-      store_row_fp6<D, C>(reinterpret_cast<uint32_t*>(kcode + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (3 * D / 4)),
-                          code, lane, cbuf[wave]);
+      for (int x = 0; x < CPL; ++x) {
+        const int c = CPL * li + x;
+        const float val = j < s.kv_len ? ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c] : 0.0f;
+        code[x] = int4_code(val, inv);
+      }
+      store_row_fp6_16<D>(reinterpret_cast<uint32_t*>(kcode + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (3 * D / 4)),
+                          code, li);
     }
     if (lane == 0)
       ws_ptr<float>(a, a.lay.sk)[(int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16 + 4 * t + wave] = scale;
@@ -270,27 +306,30 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
 }
 
 // ---- correction table: delta[qb][j] = (qbar_qb . ktilde_j) * sm_scale * log2(e) ---------------
-// Q smoothing removes each block's mean from the INT4 product; this adds back its exact share
-// (fp64 sum in channel order, one rounding to f32). grid (64-key tiles, H_kv, B), block 256:
-// lanes are keys; each wave takes NP (q head, Q block) pairs of the kv head at a time and runs
-// their NP sums side by side (independent fp64 chains, each still in channel order). Entries a
-// causal mask hides from every row of the block are written as 0.
+// Q smoothing removes each block's mean from the INT4 product; this adds back its exact share:
+// an fp64 fused multiply-add chain over the channels in order, scaled and rounded once to f32.
+// grid (64-key tiles, H_kv, B), block 256: lanes are keys (k̃ rows in LDS with a 4-float skew, so
+// a lane's 16-byte reads of its own row hit distinct banks); each wave takes NP (q head, Q block)
+// pairs per round and runs their NP chains side by side, the means coming in as uniform fp64
+// scalar operands. Entries a causal mask hides from every row of the block are written as 0.
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_delta(KArgs a) {
   constexpr int NP = 4;
+  constexpr int KS = D + 4;  // floats per k̃ row in LDS
   const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Seq s = load_seq(a, b);
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
   if (t * kKVTile >= kvpad) return;
-  __shared__ float kt[kKVTile][D + 1];
+  __shared__ __attribute__((aligned(16))) float kt[kKVTile * KS];
   const float* kbar = ws_ptr<float>(a, a.lay.kbar) + ((int64_t)b * a.Hkv + g) * D;
   for (int idx = tid; idx < kKVTile * D; idx += 256) {
     const int key = idx / D, c = idx % D;
     const int j = t * kKVTile + key;
     float val = 0.0f;
     if (j < s.kv_len) val = ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c];
-    kt[key][c] = val;
+    kt[key * KS + c] = val;
   }
   __syncthreads();
   const int grp = a.Hq / a.Hkv;
@@ -299,29 +338,34 @@ __global__ __launch_bounds__(256) void k_delta(KArgs a) {
   const int j = t * kKVTile + lane;
   const double L = (double)a.L;
   float* delta = ws_ptr<float>(a, a.lay.delta);
-  const float* qbar_all = ws_ptr<float>(a, a.lay.qbar);
+  const double* qbar64 = ws_ptr<double>(a, a.lay.qbar64);
+  const float* kr = kt + lane * KS;
   for (int p0 = wave * NP; p0 < npairs; p0 += 4 * NP) {
-    const float* qb_ptr[NP];
+    const double* qp[NP];
     int64_t out[NP];
-    bool live[NP];
+    bool live[NP], any = false;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int pair = min(p0 + u, npairs - 1);
       const int h = g * grp + pair / nqb, qb = pair % nqb;
-      qb_ptr[u] = qbar_all + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D;
+      qp[u] = qbar64 + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D;
       out[u] = (int64_t)h * a.lay.delta_len + s.delta0 + (int64_t)qb * kvpad + j;
       int jmax = s.kv_len - 1;
       if (a.causal) jmax = min(jmax, min(s.q_len, (qb + 1) * kQBlock) - 1 + (s.kv_len - s.q_len));
       live[u] = p0 + u < npairs && j <= jmax;
+      any |= live[u];
     }
     double acc[NP];
 #pragma unroll
     for (int u = 0; u < NP; ++u) acc[u] = 0.0;
-    if (live[0] || live[1] || live[2] || live[3]) {
-      for (int c = 0; c < D; ++c) {
-        const double kv = (double)kt[lane][c];
+    if (__any(any)) {
+      for (int c = 0; c < D; c += 4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(kr + c);
+        const double kv[4] = {(double)k4.x, (double)k4.y, (double)k4.z, (double)k4.w};
 #pragma unroll
-        for (int u = 0; u < NP; ++u) acc[u] += (double)qb_ptr[u][c] * kv;
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int u = 0; u < NP; ++u) acc[u] = __builtin_fma(qp[u][c + e], kv[e], acc[u]);
       }
     }
 #pragma unroll
