@@ -186,7 +186,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   constexpr int NC6 = D / 64;   // fp6 MFMAs per 32-key subtile (64 channels each)
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
   using S = Stage<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::BYTES];
+  // two separate stage arrays (not one array with offsets): the compiler then knows that the DMA
+  // filling one stage never aliases the LDS reads of the other, and does not wait on it early
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[S::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[S::BYTES];
 
   const int b = blockIdx.y;
   const int nqb_grid = (a.Nq + kQBlock - 1) / kQBlock;
@@ -243,16 +246,15 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) vofs[cb][h2][u] = S::V_OFF + 16 * v_block<D>(h2, 32 * cb + n, 2 * hh + u);
 
-  if (nt > 0) issue_tile<D>(plan, wave, lane, 0, smem, kcode, v8, drow, skp);
+  if (nt > 0) issue_tile<D>(plan, wave, lane, 0, stage0, kcode, v8, drow, skp);
   wait_dma();
   __syncthreads();
 
-#pragma unroll 1
-  for (int t = 0; t < nt; ++t) {
-    uint8_t* st = smem + (t & 1) * S::BYTES;
+  // one tile: DMA of tile t+1 into `nxt`, compute of tile t from `st`, wait, barrier
+  auto step = [&](const int t, uint8_t* st, uint8_t* nxt) __attribute__((always_inline)) {
     // next tile: DMA into the other stage (last read before the previous barrier); it has this
     // whole iteration to land
-    if (t + 1 < nt) issue_tile<D>(plan, wave, lane, t + 1, smem + ((t + 1) & 1) * S::BYTES, kcode, v8, drow, skp);
+    if (t + 1 < nt) issue_tile<D>(plan, wave, lane, t + 1, nxt, kcode, v8, drow, skp);
     if (t < nt_w) {
       // the wave needs masking only on a ragged last tile or where the causal edge crosses
       const bool need_mask = (t * kBN + kBN > s.kv_len) ||
@@ -330,6 +332,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
     }
     wait_dma();
     __syncthreads();
+  };
+#pragma unroll 1
+  for (int t = 0; t < nt; t += 2) {
+    step(t, stage0, stage1);
+    if (t + 1 < nt) step(t + 1, stage1, stage0);
   }
 
   lsum += __shfl_xor(lsum, 32, 64);
