@@ -211,12 +211,14 @@ int orc_quantize(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int fl
     }
   });
 
-  parallel_for(Hq, nthreads, [&](int h) {
+  // Q side: every (q head, Q block) unit is independent.
+  parallel_for(Hq * nqb, nthreads, [&](int unit) {
+    const int h = unit / nqb, b = unit % nqb;
     const float* Q = q + (size_t)h * Lq * d;
     const int g = h / (Hq / Hkv);  // consecutive q heads share a kv head
     const float* KT = ktil.data() + (size_t)g * Lkv * d;
     std::vector<float> qt(d);
-    for (int b = 0; b < nqb; ++b) {
+    {
       const int i0 = b * kQBlock, i1 = std::min(Lq, i0 + kQBlock);
       float* qb = qbar + ((size_t)h * nqb + b) * d;
       // 2. Q block mean over the block's valid rows (fp64 sum in row order).

@@ -265,12 +265,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
       for (int sub = 0; sub < 4; ++sub) {
         v16f acc = v16f{};
         if constexpr (D == 128) {
-          // this lane's 48 bytes of the key row (rows keep their 3-block halves contiguous)
+          // this lane's 48 bytes of the key row (rows keep their 3-block halves contiguous), read
+          // as 16+8 and 8+16 bytes so each 24-byte operand lands in one register tuple
           const uint4 b0 = *reinterpret_cast<const uint4*>(st + kofs[sub]);
-          const uint4 b1 = *reinterpret_cast<const uint4*>(st + kofs[sub] + 16);
-          const uint4 b2 = *reinterpret_cast<const uint4*>(st + kofs[sub] + 32);
+          const uint2 b1 = *reinterpret_cast<const uint2*>(st + kofs[sub] + 16);
+          const uint2 b2 = *reinterpret_cast<const uint2*>(st + kofs[sub] + 24);
+          const uint4 b3 = *reinterpret_cast<const uint4*>(st + kofs[sub] + 32);
           const v8i k0 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, 0, 0};
-          const v8i k1 = {(int)b1.z, (int)b1.w, (int)b2.x, (int)b2.y, (int)b2.z, (int)b2.w, 0, 0};
+          const v8i k1 = {(int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y, (int)b3.z, (int)b3.w, 0, 0};
           acc = mfma_fp6(k0, qop[0], acc);
           acc = mfma_fp6(k1, qop[NC6 - 1], acc);
         } else {
@@ -312,7 +314,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
       v8i pop[2];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int w = cvt_fp8x2(x[4 * q], x[4 * q + 1], 0, false);
+        // bytes 2-3 of the first conversion's "old" operand are overwritten by the second
+        const int w = cvt_fp8x2(x[4 * q], x[4 * q + 1], __float_as_int(x[4 * q]), false);
         pop[q >> 3][q & 7] = cvt_fp8x2(x[4 * q + 2], x[4 * q + 3], w, true);
       }
 #pragma unroll
