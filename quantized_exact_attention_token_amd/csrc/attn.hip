@@ -24,7 +24,10 @@
 //    The fp8 MFMA's internal accumulation is not exact FP32 on gfx950 (measured error up to about
 //    2^-11 of the largest product's binade per instruction), so each tile's product is formed from
 //    zero, accumulated in the MFMA over the tile's two 64-key halves, and folded into the FP32
-//    output registers: O = alpha*O + inner (two-level accumulation).
+//    output registers (two-level accumulation). The FP32 buffer is kept in a fixed reference
+//    frame, o = O * 2^(ref - mb): the fold is o += 2^(mb - ref) * inner (an in-place fused
+//    multiply-add, the same as rescaling O by alpha = 2^(m_prev - m) up to f32 rounding), and o, l
+//    are renormalized only when that factor would pass 2^64. The frame cancels in O = o / l.
 //  - epilogue: O * s_v / l, rounded to the output dtype.
 #include "device_common.h"
 
@@ -32,12 +35,23 @@ namespace sage2 {
 namespace {
 
 constexpr float kLog2_448 = 8.80735492205760410750f;
+// largest fold factor exponent before the running output is renormalized: o and l then stay below
+// 2^(64 + 27) for any sequence the ABI accepts
+constexpr float kFrameLimit = 64.0f;
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// max over lanes l and l ^ 32 (the two half-waves hold the two key halves of a query's row):
+// v_permlane32_swap exchanges the half-waves, and whichever of its two results holds the other
+// half's value, the max over both and the lane's own value is the pair max
+__device__ inline float half_wave_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
 template <int OUT>
@@ -80,7 +94,8 @@ constexpr int kBN = 128;  // keys per tile of the online softmax
 //    rows of 3 blocks already do.
 //  - V: two 64-key tiles, D channels x 4 blocks (the layout of the workspace's v8 tiles), block j
 //    of channel c at 4c + (j ^ ((c>>2)&3)).
-//  - the tile's 128 correction values and its 8 K group scales, contiguous.
+//  - the tile's 128 correction values and its 8 K group scales, contiguous, in a 1 KB region
+//    written by one full-wave DMA (lanes past the 34 that carry data refetch correction values).
 template <int D>
 struct Stage {
   static constexpr int CB = 3 * D / 4;         // bytes of one packed code row
@@ -91,7 +106,7 @@ struct Stage {
   static constexpr int V_OFF = KB * 16;
   static constexpr int D_OFF = V_OFF + VB * 16;
   static constexpr int S_OFF = D_OFF + kBN * 4;
-  static constexpr int BYTES = S_OFF + 32;
+  static constexpr int BYTES = D_OFF + 1024;
   static constexpr int K_INSTR = KB / 64;      // DMA instructions per region (64 blocks each)
   static constexpr int V_INSTR = VB / 64;
 };
@@ -153,10 +168,11 @@ __device__ inline void issue_tile(const DmaPlan<D>& pl, int wave, int lane, int 
 #pragma unroll
   for (int u = 0; u < (S::V_INSTR + 3) / 4; ++u)
     if (wave + 4 * u < S::V_INSTR) dma16(vt + pl.v[u], st + S::V_OFF + (wave + 4 * u) * 1024);
-  if (wave == 0 && lane < 34) {
-    const void* src = lane < 32 ? (const void*)(drow + t * kBN + 4 * lane)
-                                : (const void*)(skp + 8 * t + 4 * (lane - 32));
-    dma16(src, st + S::D_OFF);
+  if (wave == 0) {
+    // one select of two in-bounds addresses (no divergent branch around the DMA)
+    const float* dsrc = drow + t * kBN + 4 * (lane & 31);
+    const float* ssrc = skp + 8 * t + 4 * (lane & 1);
+    dma16((unsigned)(lane - 32) < 2u ? ssrc : dsrc, st + S::D_OFF);
   }
 }
 
@@ -195,7 +211,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const int nqb_grid = (a.Nq + kQBlock - 1) / kQBlock;
   int qb, h;
   decode_work(blockIdx.x, nqb_grid, a.Hq, a.Hq / a.Hkv, &qb, &h);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+  // the wave index in an SGPR: the DMA share of each wave is then decided by scalar code
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63,
+            n = lane & 31, hh = lane >> 5;
+  __builtin_assume(wave >= 0 && wave < 4);
   const Seq s = load_seq(a, b);
   if (qb * kQBlock >= s.q_len) return;
   const int g = h / (a.Hq / a.Hkv);
@@ -228,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const float* drow = ws_ptr<float>(a, a.lay.delta) + (int64_t)h * a.lay.delta_len + s.delta0 +
                       (int64_t)qb * kvpad;
 
-  float m = kNegInf, lsum = 0.0f;
+  float m = kNegInf, lsum = 0.0f, ref = 0.0f;
   v16f o[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{};
@@ -300,17 +319,30 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
       float mt = x[0];
 #pragma unroll
       for (int k = 1; k < 64; ++k) mt = fmaxf(mt, x[k]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = half_wave_max(mt);
       const float mnew = fmaxf(m, mt);
-      const float alpha = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
       const float mb = (mnew == kNegInf) ? 0.0f : mnew - kLog2_448;
+      // the output frame starts at the first tile with a visible key; renormalize (rarely) before
+      // the fold factor 2^(mb - ref) could leave the f32 range
+      if (m == kNegInf) ref = mb;
+      if (__any(mb - ref > kFrameLimit)) {
+        const float r = __builtin_amdgcn_exp2f(ref - mb);
+        lsum *= r;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[cb][e] *= r;
+        ref = mb;
+      }
+      const float factor = __builtin_amdgcn_exp2f(mb - ref);
+      // (each exp is followed by independent adds: the transcendental unit then overlaps them)
       float ps = 0.0f;
 #pragma unroll
       for (int k = 0; k < 64; ++k) {
         x[k] = __builtin_amdgcn_exp2f(x[k] - mb);
         ps += x[k];
       }
-      lsum = alpha * lsum + ps;
+      lsum = __builtin_fmaf(ps, factor, lsum);
       v8i pop[2];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -329,7 +361,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
           inner = mfma_fp8(vop, pop[h2], inner);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(alpha, o[cb][r], inner[r]);
+        for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(inner[r], factor, o[cb][r]);
       }
       m = mnew;
     }

@@ -12,8 +12,11 @@ section "Channel Outlier Smoothing": a few channels dominate the range).
 Draw order, all from one CPU torch.Generator seeded per workload: standard normal fp32 Q
 [B, Nq, Hq, d], then K [B, Nkv, Hkv, d], then V, then the outlier channel indices (randperm(d)[:n]
 per kv head), then the offset vectors. Outliers multiply the chosen channels of Q and K (the same
-channels for a kv head and every q head that shares it) before any offset is added. The result is
-rounded to the input dtype (round to nearest even).
+channels for a kv head and every q head that shares it) before any offset is added. Optional
+deterministic terms follow (no random draws): `key_ramp` adds key_ramp * j / Nkv to every channel
+of key j, and `q_shift` adds a constant to every channel of Q, so the logits of a row climb
+steadily along the keys (a row whose running max keeps rising). The result is rounded to the input
+dtype (round to nearest even).
 """
 from __future__ import annotations
 
@@ -40,6 +43,8 @@ class Workload:
     n_outliers: int = 0
     outlier_scale: float = 1.0
     seqlens: list | None = None     # packed variable-length batch: per-sequence lengths (Nq == Nkv)
+    key_ramp: float = 0.0           # K[j] += key_ramp * j / Nkv (all channels)
+    q_shift: float = 0.0            # Q += q_shift (all channels)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -79,6 +84,10 @@ def generate(w: Workload):
     if w.k_offset_rademacher:
         sign = torch.randint(0, 2, (w.Hkv, w.d), generator=g).float() * 2 - 1
         k += (sign * w.k_offset_rademacher)[None, None]
+    if w.key_ramp:
+        k += (torch.arange(Nkv, dtype=torch.float32) * (w.key_ramp / Nkv))[None, :, None, None]
+    if w.q_shift:
+        q += w.q_shift
     q, k, v = q.to(w.dtype), k.to(w.dtype), v.to(w.dtype)
     if w.varlen:
         cu = torch.zeros(len(w.seqlens) + 1, dtype=torch.int32)

@@ -93,3 +93,21 @@ def test_varlen_equals_separate_calls():
         o = sage2.attention(q, k, v, causal=True)
         torch.cuda.synchronize()
         assert torch.equal(o[0].view(torch.int16), packed[s:e].view(torch.int16)), i
+
+
+@pytest.mark.parametrize("case", [(64, torch.float16, False), (128, torch.bfloat16, True)],
+                         ids=["d64_full", "d128_causal"])
+def test_rising_row_max_renormalizes(case):
+    """Logits that climb by hundreds (base 2) along the keys: the running max keeps rising, so the
+    kernel's FP32 output buffer is renormalized several times on the way (its fold factor would
+    otherwise pass 2^64). The result must still match the oracle."""
+    import oracle as O
+    d, dt, causal = case
+    w = W.custom(1, 2, 1, 512, 512, d, dt, causal, seed=11 + d, key_ramp=8.0, q_shift=4.0)
+    run = _full_check(w)
+    q, k, v = run.seq_inputs(0)
+    z = O.quantize(q, k, v)
+    x = O.logits(z, causal, rows=np.array([511], np.int32))[:, 0]
+    span = float((x.max(axis=-1) - x.min(axis=-1)).min())
+    assert span > 3 * 64, f"logit span {span} too small to reach the renormalization"
+
