@@ -99,7 +99,9 @@ typedef struct {
  *                                             tile, channel c, half h, slot s holds key
  *                                             32*(s/16) + 8*((s%16)/4) + 4*h + s%4
  *   delta      f32   [H_q][delta_len]         correction (qbar . smoothed k_j) * sm_scale * log2(e),
- *                                             per sequence a [q_blocks][kv_rows] block at delta0
+ *                                             per sequence a [q_blocks][kv_rows] block at delta0;
+ *                                             entries of keys a causal mask hides from every row
+ *                                             of the Q block are unspecified
  */
 typedef struct {
   int64_t total_bytes;

@@ -308,14 +308,22 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
 // ---- correction table: delta[qb][j] = (qbar_qb . ktilde_j) * sm_scale * log2(e) ---------------
 // Q smoothing removes each block's mean from the INT4 product; this adds back its exact share:
 // an fp64 fused multiply-add chain over the channels in order, scaled and rounded once to f32.
-// grid (64-key tiles, H_kv, B), block 256: lanes are keys (k̃ rows in LDS with a 4-float skew, so
-// a lane's 16-byte reads of its own row hit distinct banks); each wave takes NP (q head, Q block)
-// pairs per round and runs their NP chains side by side, the means coming in as uniform fp64
-// scalar operands. Entries a causal mask hides from every row of the block are written as 0.
+// The chains run on v_mfma_f64_16x16x4_f64: on gfx950 it accumulates every output as four fused
+// multiply-adds in k order on top of C (checked bit for bit against sequential fma() on
+// cancellation-heavy inputs), so feeding it the channels four at a time, in order, is exactly
+// the channel-order chain. Operand layouts: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k,
+// D[i][j] in lane j + 16 (i % 4), register i / 4.
+// grid (64-key tiles, H_kv, B), block 256: k~ of the tile in LDS (f32, a 4-float row skew). Only
+// the (q head, Q block) pairs that see a key of the tile are computed: they are numbered Q block
+// major and dealt to the waves in blocks of 32 pairs x the 64 keys = 2 x 4 MFMA tiles, so a causal
+// mask leaves no wave idle. Entries a causal mask hides from every row of a Q block are left
+// unwritten (the attention kernel masks such keys by selection, never reads them into arithmetic
+// that reaches the output) except within a computed tile, where they are stored as 0.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_delta(KArgs a) {
-  constexpr int NP = 4;
-  constexpr int KS = D + 4;  // floats per k̃ row in LDS
+  constexpr int KS = D + 4;  // floats per k~ row in LDS
   const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -335,42 +343,92 @@ __global__ __launch_bounds__(256) void k_delta(KArgs a) {
   const int grp = a.Hq / a.Hkv;
   const int nqb = (s.q_len + kQBlock - 1) / kQBlock;
   const int npairs = grp * nqb;
-  const int j = t * kKVTile + lane;
+  const int koff = s.kv_len - s.q_len;
+  const int li = lane & 15, lk = lane >> 4;
   const double L = (double)a.L;
   float* delta = ws_ptr<float>(a, a.lay.delta);
   const double* qbar64 = ws_ptr<double>(a, a.lay.qbar64);
-  const float* kr = kt + lane * KS;
-  for (int p0 = wave * NP; p0 < npairs; p0 += 4 * NP) {
-    const double* qp[NP];
-    int64_t out[NP];
-    bool live[NP], any = false;
+  // last key that any row of Q block qb sees
+  auto jmax_of = [&](int qb) {
+    int jm = s.kv_len - 1;
+    if (a.causal) jm = min(jm, min(s.q_len, (qb + 1) * kQBlock) - 1 + koff);
+    return jm;
+  };
+  // first Q block that sees a key of this tile (jmax_of is non-decreasing in qb)
+  int qbmin;
+  if (t * kKVTile >= s.kv_len) {
+    qbmin = nqb;
+  } else if (!a.causal) {
+    qbmin = 0;
+  } else {
+    const int T = t * kKVTile + 1 - koff;  // needs min(q_len, (qb + 1) * 128) >= T
+    qbmin = T <= 0 ? 0 : (T > s.q_len ? nqb : (T + kQBlock - 1) / kQBlock - 1);
+  }
+  // live pairs, Q-block major: pair p -> Q block qbmin + p / grp, q head g * grp + p % grp;
+  // blocks of 32 pairs go round-robin to the waves
+  const int nlive = (nqb - qbmin) * grp;
+  for (int p0 = 32 * wave; p0 < nlive; p0 += 128) {
+    const double* qrow[2];
 #pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int pair = min(p0 + u, npairs - 1);
-      const int h = g * grp + pair / nqb, qb = pair % nqb;
-      qp[u] = qbar64 + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D;
-      out[u] = (int64_t)h * a.lay.delta_len + s.delta0 + (int64_t)qb * kvpad + j;
-      int jmax = s.kv_len - 1;
-      if (a.causal) jmax = min(jmax, min(s.q_len, (qb + 1) * kQBlock) - 1 + (s.kv_len - s.q_len));
-      live[u] = p0 + u < npairs && j <= jmax;
-      any |= live[u];
+    for (int rb = 0; rb < 2; ++rb) {
+      const int pc = min(p0 + 16 * rb + li, nlive - 1);
+      const int h = g * grp + pc % grp, qb = qbmin + pc / grp;
+      qrow[rb] = qbar64 + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + lk;
     }
-    double acc[NP];
+    v4d acc[2][4];
 #pragma unroll
-    for (int u = 0; u < NP; ++u) acc[u] = 0.0;
-    if (__any(any)) {
-      for (int c = 0; c < D; c += 4) {
-        const float4 k4 = *reinterpret_cast<const float4*>(kr + c);
-        const double kv[4] = {(double)k4.x, (double)k4.y, (double)k4.z, (double)k4.w};
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+      for (int kb = 0; kb < 4; ++kb) acc[rb][kb] = v4d{0.0, 0.0, 0.0, 0.0};
+    // channels in chunks of 16 (4 MFMA k-steps); the next chunk's means are requested before the
+    // current chunk's MFMAs, so their latency hides behind 32 MFMAs
+    // (rows of pairs past the end read the clamped last pair: an output row depends only on its
+    // own A row, and those rows are never stored)
+    double a_cur[4][2], a_nxt[4][2];
 #pragma unroll
-          for (int u = 0; u < NP; ++u) acc[u] = __builtin_fma(qp[u][c + e], kv[e], acc[u]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = qrow[rb][4 * u];
+    const float* kr = kt + li * KS + lk;
+#pragma unroll 1
+    for (int ch = 0; ch < D; ch += 16) {
+      const int nx = ch + 16 < D ? ch + 16 : 0;  // (the last prefetch rereads chunk 0, unused)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) a_nxt[u][rb] = qrow[rb][nx + 4 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        double bv[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) bv[kb] = (double)kr[16 * kb * KS + ch + 4 * u];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            acc[rb][kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a_cur[u][rb], bv[kb], acc[rb][kb], 0, 0, 0);
       }
-    }
 #pragma unroll
-    for (int u = 0; u < NP; ++u)
-      if (p0 + u < npairs) delta[out[u]] = live[u] ? (float)(acc[u] * L) : 0.0f;
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = a_nxt[u][rb];
+    }
+    // D[i][j]: pair p0 + 16 rb + lk + 4 r, key t*64 + 16 kb + li
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pair = p0 + 16 * rb + lk + 4 * r;
+        if (pair >= nlive) continue;
+        const int h = g * grp + pair % grp, qb = qbmin + pair / grp;
+        const int jm = jmax_of(qb);
+        float* drow = delta + (int64_t)h * a.lay.delta_len + s.delta0 + (int64_t)qb * kvpad;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int j = t * kKVTile + 16 * kb + li;
+          drow[j] = j <= jm ? (float)(acc[rb][kb][r] * L) : 0.0f;
+        }
+      }
   }
 }
 
