@@ -51,50 +51,163 @@ __global__ void k_plan(KArgs a) {
   }
 }
 
+// Widening of one raw fp16 / bf16 element (exact).
+template <int IN>
+__device__ inline float widen16(uint32_t raw) {
+  if constexpr (IN == SAGE2_BF16) {
+    return __uint_as_float(raw << 16);
+  } else {
+    _Float16 h;
+    const uint16_t r16 = (uint16_t)raw;
+    __builtin_memcpy(&h, &r16, 2);
+    return (float)h;
+  }
+}
+
+// The 8 elements of a 16-byte chunk, widened.
+template <int IN>
+__device__ inline void widen8(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = widen16<IN>(w[e] & 0xFFFFu);
+    f[2 * e + 1] = widen16<IN>(w[e] >> 16);
+  }
+}
+
+// Rows [tok0, tok0 + n) of one head of a strided input, as 16-byte chunks for a block of 256
+// threads: chunk k of thread x is row (x + 256 k) / (D/8), channels 8 ((x + 256 k) % (D/8)) + [0, 8).
+// All of a thread's loads are issued before any is waited on; rows n..NROWS-1 are zero (they reread
+// row n-1, which exists whenever n > 0, and are then cleared).
+template <int D, int NROWS>
+__device__ inline void load_rows(uint4 (&v)[NROWS * D / 8 / 256], const void* base, const int64_t* strides,
+                                 int b, int64_t tok0, int head, int n) {
+  constexpr int RW = D / 8;
+  constexpr int IT = NROWS * RW / 256;
+  static_assert(NROWS * RW % 256 == 0, "tile must split evenly over the block");
+#pragma unroll
+  for (int k = 0; k < IT; ++k) v[k] = make_uint4(0, 0, 0, 0);
+  if (n > 0) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int idx = threadIdx.x + 256 * k, r = idx / RW, ch = idx % RW;
+      v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) +
+                                             row_index(strides, b, tok0 + min(r, n - 1), head) + 8 * ch);
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+      if ((threadIdx.x + 256 * k) / RW >= n) v[k] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// The same rows, raw, into LDS rows of D elements.
+template <int D, int NROWS>
+__device__ inline void stage_rows(uint16_t (*dst)[D], const void* base, const int64_t* strides, int b,
+                                  int64_t tok0, int head, int n) {
+  constexpr int RW = D / 8;
+  uint4 v[NROWS * RW / 256];
+  load_rows<D, NROWS>(v, base, strides, b, tok0, head, n);
+#pragma unroll
+  for (int k = 0; k < NROWS * RW / 256; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    *reinterpret_cast<uint4*>(&dst[idx / RW][8 * (idx % RW)]) = v[k];
+  }
+}
+
 // ---- K channel sums and V channel max over one 128-token chunk ---------------------------------
-// grid (chunks, H_kv, B), block D threads: thread c sums channel c over the chunk in token order.
+// grid (chunks, H_kv, B), block 256. The chunk's K rows are staged in LDS (zero rows past the
+// sequence end add +0.0, which leaves an fp64 sum unchanged); threads c < D then sum channel c in
+// token order. V's channel max needs no order: each thread keeps the max of the 8 channels it
+// loads, and threads D..2D-1 combine them.
 template <int D, int IN>
-__global__ __launch_bounds__(D) void k_kstats(KArgs a) {
-  const int u = blockIdx.x, g = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+__global__ __launch_bounds__(256) void k_kstats(KArgs a) {
+  constexpr int RW = D / 8;
+  constexpr int RPP = 256 / RW;  // rows per pass of the block over the chunk
+  const int u = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const Seq s = load_seq(a, b);
   if (u * kKVPad >= s.kv_len) return;
-  const int j0 = u * kKVPad, j1 = min(s.kv_len, j0 + kKVPad);
-  double part = 0.0;
-  float vmax = 0.0f;
-  for (int j = j0; j < j1; ++j) {
-    part += (double)ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c);
-    vmax = fmaxf(vmax, fabsf(ld_in<IN>(a.v, row_index(a.vs, b, s.kv_start + j, g) + c)));
+  const int j0 = u * kKVPad, n = min(kKVPad, s.kv_len - j0);
+  __shared__ __attribute__((aligned(16))) uint16_t kr[kKVPad][D];
+  __shared__ float vm[RPP][D];
+  stage_rows<D, kKVPad>(kr, a.k, a.ks, b, s.kv_start + j0, g, n);
+  {
+    // V: this thread's chunks all share channels 8 (tid % RW) + [0, 8) (256 is a multiple of RW)
+    const int ch = tid % RW, r0 = tid / RW;
+    uint4 v[kKVPad * RW / 256];
+    load_rows<D, kKVPad>(v, a.v, a.vs, b, s.kv_start + j0, g, n);
+    float m8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kKVPad * RW / 256; ++k) {
+      float f[8];
+      widen8<IN>(v[k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m8[e] = fmaxf(m8[e], fabsf(f[e]));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vm[r0][8 * ch + e] = m8[e];
   }
-  const int64_t slot = ((int64_t)g * (a.lay.kv_rows / kKVPad) + s.kv_row0 / kKVPad + u) * D + c;
-  ws_ptr<double>(a, a.lay.k_partial)[slot] = part;
-  ws_ptr<float>(a, a.lay.v_partial)[slot] = vmax;
+  __syncthreads();
+  const int64_t slot0 = ((int64_t)g * (a.lay.kv_rows / kKVPad) + s.kv_row0 / kKVPad + u) * D;
+  if (tid < D) {
+    double part = 0.0;
+#pragma unroll 16
+    for (int i = 0; i < kKVPad; ++i) part += (double)widen16<IN>(kr[i][tid]);
+    ws_ptr<double>(a, a.lay.k_partial)[slot0 + tid] = part;
+  } else if (tid < 2 * D) {
+    const int c = tid - D;
+    float vmax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) vmax = fmaxf(vmax, vm[r][c]);
+    ws_ptr<float>(a, a.lay.v_partial)[slot0 + c] = vmax;
+  }
 }
 
 // ---- K mean and V scale: chunks reduced in order -----------------------------------------------
+// grid (D/32 channel groups, H_kv, B), block 256: the chunk partials of 32 channels are brought
+// into LDS 64 chunks at a time (8 loads in flight per thread), then 32 threads add them in chunk
+// order (missing chunks past the end add +0.0).
 template <int D>
-__global__ __launch_bounds__(D) void k_kreduce(KArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(256) void k_kreduce(KArgs a) {
+  const int cg = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int cl = tid & 31, rr = tid >> 5;
   const Seq s = load_seq(a, b);
-  const int64_t out = ((int64_t)b * a.Hkv + g) * D + c;
-  float kbar = 0.0f, sv = 0.0f, svinv = 0.0f;
-  if (s.kv_len > 0) {
-    const int nch = (s.kv_len + kKVPad - 1) / kKVPad;
-    const int64_t base = ((int64_t)g * (a.lay.kv_rows / kKVPad) + s.kv_row0 / kKVPad) * D + c;
-    double total = 0.0;
-    float amax = 0.0f;
-    for (int u = 0; u < nch; ++u) {
-      total += ws_ptr<double>(a, a.lay.k_partial)[base + (int64_t)u * D];
-      amax = fmaxf(amax, ws_ptr<float>(a, a.lay.v_partial)[base + (int64_t)u * D]);
+  __shared__ double kp[64][32];
+  __shared__ float vp[64][32];
+  const int nch = (s.kv_len + kKVPad - 1) / kKVPad;
+  const int64_t base = ((int64_t)g * (a.lay.kv_rows / kKVPad) + s.kv_row0 / kKVPad) * D + 32 * cg + cl;
+  double total = 0.0;
+  float amax = 0.0f;
+  for (int u0 = 0; u0 < nch; u0 += 64) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int u = u0 + rr + 8 * k;
+      kp[rr + 8 * k][cl] = u < nch ? ws_ptr<double>(a, a.lay.k_partial)[base + (int64_t)u * D] : 0.0;
+      vp[rr + 8 * k][cl] = u < nch ? ws_ptr<float>(a, a.lay.v_partial)[base + (int64_t)u * D] : 0.0f;
     }
-    kbar = (float)(total / (double)s.kv_len);
-    if (amax != 0.0f) {
-      sv = amax / 448.0f;     // V channel amax maps to 448, the largest e4m3 value
-      svinv = 448.0f / amax;
+    __syncthreads();
+    if (tid < 32) {
+#pragma unroll 16
+      for (int k = 0; k < 64; ++k) {
+        total += kp[k][tid];
+        amax = fmaxf(amax, vp[k][tid]);
+      }
     }
+    __syncthreads();
   }
-  ws_ptr<float>(a, a.lay.kbar)[out] = kbar;
-  ws_ptr<float>(a, a.lay.sv)[out] = sv;
-  ws_ptr<float>(a, a.lay.sv_inv)[out] = svinv;
+  if (tid < 32) {
+    const int64_t out = ((int64_t)b * a.Hkv + g) * D + 32 * cg + tid;
+    float kbar = 0.0f, sv = 0.0f, svinv = 0.0f;
+    if (s.kv_len > 0) {
+      kbar = (float)(total / (double)s.kv_len);
+      if (amax != 0.0f) {
+        sv = amax / 448.0f;     // V channel amax maps to 448, the largest e4m3 value
+        svinv = 448.0f / amax;
+      }
+    }
+    ws_ptr<float>(a, a.lay.kbar)[out] = kbar;
+    ws_ptr<float>(a, a.lay.sv)[out] = sv;
+    ws_ptr<float>(a, a.lay.sv_inv)[out] = svinv;
+  }
 }
 
 // INT4 code of x given the group's inverse scale: round to nearest even, clamp to [-7, 7].
@@ -151,39 +264,26 @@ __device__ inline float max16(float x) {
 }
 
 // ---- Q: block mean, per-token INT4 codes -------------------------------------------------------
-// grid (Q blocks, H_q, B), block 256. The block's rows are read once, coalesced, into LDS; the mean
-// is an fp64 sum over the valid rows in row order (thread c: channel c); each of the 4 waves then
-// quantizes every 4th row (one scale per token: on gfx950 a lane owns one query column of the
-// S^T = K Q^T MFMA tile, so the per-thread group is one token).
+// grid (Q blocks, H_q, B), block 256. The block's rows are read once, coalesced, into LDS (rows past
+// the sequence end are zero and add +0.0 to the fp64 sums); thread c sums channel c in row order.
+// Each of the 4 waves then quantizes every 4th row, 16 lanes per row with 8 channels each (one scale
+// per token: on gfx950 a lane owns one query column of the S^T = K Q^T MFMA tile, so the
+// per-thread group is one token).
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
-  constexpr int RW = D / 8;  // 16-byte chunks per row
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seq s = load_seq(a, b);
   if (qb * kQBlock >= s.q_len) return;
   const int i0 = qb * kQBlock, n = min(kQBlock, s.q_len - i0);
   __shared__ __attribute__((aligned(16))) uint16_t rows[kQBlock][D];
-  __shared__ float qbar[D];
-  for (int idx = tid; idx < n * RW; idx += 256) {
-    const int r = idx / RW, ch = idx % RW;
-    const uint4 v = *reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(a.q) + row_index(a.qs, b, s.q_start + i0 + r, h) + 8 * ch);
-    *reinterpret_cast<uint4*>(&rows[r][8 * ch]) = v;
-  }
+  __shared__ __attribute__((aligned(16))) float qbar[D];
+  stage_rows<D, kQBlock>(rows, a.q, a.qs, b, s.q_start + i0, h, n);
   __syncthreads();
-  auto widen = [](uint16_t raw) {
-    if constexpr (IN == SAGE2_BF16) {
-      return __uint_as_float((uint32_t)raw << 16);
-    } else {
-      _Float16 hv;
-      __builtin_memcpy(&hv, &raw, 2);
-      return (float)hv;
-    }
-  };
   if (tid < D) {
     double sum = 0.0;
-    for (int i = 0; i < n; ++i) sum += (double)widen(rows[i][tid]);
+#pragma unroll 16
+    for (int i = 0; i < kQBlock; ++i) sum += (double)widen16<IN>(rows[i][tid]);
     const float m = (float)(sum / (double)n);
     qbar[tid] = m;
     const int64_t at = ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + tid;
@@ -193,18 +293,28 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
   __syncthreads();
   uint8_t* qcode = ws_ptr<uint8_t>(a, a.lay.qcode);
   float* sq = ws_ptr<float>(a, a.lay.sq);
-  constexpr int CPL = D / 16;
+  constexpr int CPL = D / 16;  // channels per lane: 8 (D = 128) or 4 (D = 64)
   const int li = lane & 15;
+  float qm[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) qm[e] = qbar[CPL * li + e];
+#pragma unroll 2
   for (int it = 0; it < 8; ++it) {
     const int r = 32 * wave + 4 * it + (lane >> 4);  // 4 rows per wave at a time, 16 lanes each
     const int64_t prow = (int64_t)h * a.lay.q_rows + s.q_row0 + i0 + r;
+    float raw[8];
+    if constexpr (CPL == 8) {
+      widen8<IN>(*reinterpret_cast<const uint4*>(&rows[r][8 * li]), raw);
+    } else {
+      const uint2 v2 = *reinterpret_cast<const uint2*>(&rows[r][4 * li]);
+      widen8<IN>(make_uint4(v2.x, v2.y, 0, 0), raw);
+    }
     int code[CPL];
     float qt[CPL];
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
-      const int c = CPL * li + e;
-      qt[e] = r < n ? widen(rows[r][c]) - qbar[c] : 0.0f;
+      qt[e] = r < n ? raw[e] - qm[e] : 0.0f;
       amax = fmaxf(amax, fabsf(qt[e]));
     }
     amax = max16(amax);
@@ -222,70 +332,86 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
 __device__ inline int tile_key(int h, int s) { return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * h + (s & 3); }
 
 // ---- K: per-16-key-group INT4 codes; V: FP8 codes in the attention kernel's tile layout -------
-// grid (64-key tiles, H_kv, B), block 256. Wave w quantizes group w of the tile: the 16 keys of
-// 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half owns).
+// grid (64-key tiles, H_kv, B), block 256. The tile's K and V rows are staged in LDS with 16-byte
+// loads (zero past the sequence end). Wave w quantizes K group w of the tile: the 16 keys of
+// 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half owns), 4 keys at a
+// time with 16 lanes per key; the smoothed values stay in registers between the group max and the
+// codes.
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
-  constexpr int C = D / 64;
+  constexpr int CPL = D / 16;  // channels per lane in a 16-lane key row
   const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seq s = load_seq(a, b);
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
   if (t * kKVTile >= kvpad) return;
-  __shared__ float kbar[D], svinv[D];
+  __shared__ __attribute__((aligned(16))) float kbar[D];
+  __shared__ float svinv[D];
+  __shared__ __attribute__((aligned(16))) uint16_t kr[kKVTile][D];
   __shared__ float vt[kKVTile][D + 1];
   const int64_t sidx = ((int64_t)b * a.Hkv + g) * D;
   if (tid < D) {
     kbar[tid] = ws_ptr<float>(a, a.lay.kbar)[sidx + tid];
     svinv[tid] = ws_ptr<float>(a, a.lay.sv_inv)[sidx + tid];
   }
+  const int n = max(0, min(kKVTile, s.kv_len - t * kKVTile));
+  stage_rows<D, kKVTile>(kr, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n);
   __syncthreads();
+  // V rows, scaled per channel (f32), into vt
+  {
+    constexpr int RW = D / 8;
+    uint4 v[kKVTile * RW / 256];
+    load_rows<D, kKVTile>(v, a.v, a.vs, b, s.kv_start + t * kKVTile, g, n);
+#pragma unroll
+    for (int k = 0; k < kKVTile * RW / 256; ++k) {
+      const int idx = tid + 256 * k, key = idx / RW, ch = idx % RW;
+      float f[8];
+      widen8<IN>(v[k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[key][8 * ch + e] = f[e] * svinv[8 * ch + e];
+    }
+  }
   // K group of this wave
   {
-    const int half = wave & 1, sub = wave >> 1;
+    const int half = wave & 1, sub = wave >> 1, li = lane & 15;
+    float km[CPL];
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) km[x] = kbar[CPL * li + x];
+    float val[4][CPL];
     float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = t * kKVTile + 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);
+    for (int it = 0; it < 4; ++it) {
+      const int e = 4 * it + (lane >> 4);
+      const int key = 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);  // within the tile
+      float raw[8];
+      if constexpr (CPL == 8) {
+        widen8<IN>(*reinterpret_cast<const uint4*>(&kr[key][8 * li]), raw);
+      } else {
+        const uint2 v2 = *reinterpret_cast<const uint2*>(&kr[key][4 * li]);
+        widen8<IN>(make_uint4(v2.x, v2.y, 0, 0), raw);
+      }
 #pragma unroll
-      for (int x = 0; x < C; ++x) {
-        const int c = lane * C + x;
-        float val = 0.0f;
-        if (j < s.kv_len) val = ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c];
-        amax = fmaxf(amax, fabsf(val));
+      for (int x = 0; x < CPL; ++x) {
+        val[it][x] = key < n ? raw[x] - km[x] : 0.0f;
+        amax = fmaxf(amax, fabsf(val[it][x]));
       }
     }
     amax = wave_max(amax);
     const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
     const float scale = amax == 0.0f ? 0.0f : amax / 7.0f;
     uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode);
-    // codes: 4 keys of the group at a time, 16 lanes per key (values re-read through L1)
-    constexpr int CPL = D / 16;
-    const int li = lane & 15;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int e = 4 * it + (lane >> 4);
       const int j = t * kKVTile + 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);
       int code[CPL];
 #pragma unroll
-      for (int x = 0; x < CPL; ++x) {
-        const int c = CPL * li + x;
-        const float val = j < s.kv_len ? ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c] : 0.0f;
-        code[x] = int4_code(val, inv);
-      }
+      for (int x = 0; x < CPL; ++x) code[x] = int4_code(val[it][x], inv);
       store_row_fp6_16<D>(reinterpret_cast<uint32_t*>(kcode + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (3 * D / 4)),
                           code, li);
     }
     if (lane == 0)
       ws_ptr<float>(a, a.lay.sk)[(int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16 + 4 * t + wave] = scale;
-  }
-  // V tile, scaled per channel, staged in LDS
-  for (int idx = tid; idx < kKVTile * D; idx += 256) {
-    const int key = idx / D, c = idx % D;
-    const int j = t * kKVTile + key;
-    float val = 0.0f;
-    if (j < s.kv_len) val = ld_in<IN>(a.v, row_index(a.vs, b, s.kv_start + j, g) + c) * svinv[c];
-    vt[key][c] = val;
   }
   __syncthreads();
   uint8_t* v8 = ws_ptr<uint8_t>(a, a.lay.v8) +
@@ -332,12 +458,20 @@ __global__ __launch_bounds__(256) void k_delta(KArgs a) {
   if (t * kKVTile >= kvpad) return;
   __shared__ __attribute__((aligned(16))) float kt[kKVTile * KS];
   const float* kbar = ws_ptr<float>(a, a.lay.kbar) + ((int64_t)b * a.Hkv + g) * D;
-  for (int idx = tid; idx < kKVTile * D; idx += 256) {
-    const int key = idx / D, c = idx % D;
-    const int j = t * kKVTile + key;
-    float val = 0.0f;
-    if (j < s.kv_len) val = ld_in<IN>(a.k, row_index(a.ks, b, s.kv_start + j, g) + c) - kbar[c];
-    kt[key * KS + c] = val;
+  {
+    // k~ = k - kbar in f32 (keys past the sequence end: 0)
+    constexpr int RW = D / 8;
+    const int n = max(0, min(kKVTile, s.kv_len - t * kKVTile));
+    uint4 v[kKVTile * RW / 256];
+    load_rows<D, kKVTile>(v, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n);
+#pragma unroll
+    for (int k = 0; k < kKVTile * RW / 256; ++k) {
+      const int idx = tid + 256 * k, key = idx / RW, ch = idx % RW;
+      float f[8];
+      widen8<IN>(v[k], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kt[key * KS + 8 * ch + e] = key < n ? f[e] - kbar[8 * ch + e] : 0.0f;
+    }
   }
   __syncthreads();
   const int grp = a.Hq / a.Hkv;
@@ -438,8 +572,8 @@ int launch_all(const KArgs& a, hipStream_t st) {
   const int nqb = (a.Nq + kQBlock - 1) / kQBlock;
   const int ntile = nch * (kKVPad / kKVTile);
   k_plan<<<1, 64, 0, st>>>(a);
-  k_kstats<D, IN><<<dim3(nch, a.Hkv, a.B), D, 0, st>>>(a);
-  k_kreduce<D><<<dim3(a.Hkv, a.B), D, 0, st>>>(a);
+  k_kstats<D, IN><<<dim3(nch, a.Hkv, a.B), 256, 0, st>>>(a);
+  k_kreduce<D><<<dim3(D / 32, a.Hkv, a.B), 256, 0, st>>>(a);
   k_quant_q<D, IN><<<dim3(nqb, a.Hq, a.B), 256, 0, st>>>(a);
   k_quant_kv<D, IN><<<dim3(ntile, a.Hkv, a.B), 256, 0, st>>>(a);
   k_delta<D, IN><<<dim3(ntile, a.Hkv, a.B), 256, 0, st>>>(a);
