@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
 // cancellation-heavy inputs), so feeding it the channels four at a time, in order, is exactly
 // the channel-order chain. Operand layouts: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k,
 // D[i][j] in lane j + 16 (i % 4), register i / 4.
-// grid (64-key tiles, H_kv, B), block 256: k~ of the tile in LDS (f32, a 4-float row skew). Only
+// grid (64-key tiles x H_kv, 1, B), block 256: k~ of the tile in LDS (f32, a 4-float row skew). Only
 // the (q head, Q block) pairs that see a key of the tile are computed: they are numbered Q block
 // major and dealt to the waves in blocks of 32 pairs x the 64 keys = 2 x 4 MFMA tiles, so a causal
 // mask leaves no wave idle. Entries a causal mask hides from every row of a Q block are left
@@ -450,7 +450,9 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_delta(KArgs a) {
   constexpr int KS = D + 4;  // floats per k~ row in LDS
-  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // blockIdx.x = tile * H_kv + kv head: under a causal mask the early key tiles carry the most
+  // (q head, Q block) pairs, and this order dispatches them first (longest first)
+  const int t = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Seq s = load_seq(a, b);
@@ -576,7 +578,7 @@ int launch_all(const KArgs& a, hipStream_t st) {
   k_kreduce<D><<<dim3(D / 32, a.Hkv, a.B), 256, 0, st>>>(a);
   k_quant_q<D, IN><<<dim3(nqb, a.Hq, a.B), 256, 0, st>>>(a);
   k_quant_kv<D, IN><<<dim3(ntile, a.Hkv, a.B), 256, 0, st>>>(a);
-  k_delta<D, IN><<<dim3(ntile, a.Hkv, a.B), 256, 0, st>>>(a);
+  k_delta<D, IN><<<dim3(ntile * a.Hkv, 1, a.B), 256, 0, st>>>(a);
   return (int)hipGetLastError();
 }
 
