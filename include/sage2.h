@@ -13,8 +13,11 @@
  *   - INT32-exact QK^T, dequantization and an online softmax;
  *   - P~ and V in FP8 (OCP e4m3), P~V on FP8 MFMA with a two-level accumulation: each short MFMA
  *     run is folded into an FP32 buffer (section "Numerical Repair Stack": periodic FP32 foldback).
- * The interface envelope (variable lengths, grouped-query heads, q/kv lengths that differ, head dim
- * 64 or 128 only, larger rejected) follows section "Implementation envelope" of the visual companion.
+ * The interface envelope (variable lengths, grouped-query heads, q/kv lengths that differ, head dims
+ * up to 128 padded to 64 or 128, larger rejected) follows section "Implementation envelope" of the
+ * visual companion. Here a head dim d is any multiple of 8 in [8, 128]; it is padded with zero
+ * channels to 64 (d <= 64) or 128 inside the workspace, which changes no code, scale, mean or
+ * correction value, and the default softmax scale uses the true d.
  *
  * Two calls do the work: sage2_quantize_smooth (the pre-pass: smoothing statistics, INT4/FP8 codes,
  * scales, correction table, written into a caller-provided workspace) and sage2_attn_fwd (the
@@ -46,13 +49,20 @@ typedef enum {
   SAGE2_OK = 0,
   SAGE2_ERR_NULL = 1,         /* a required pointer is NULL */
   SAGE2_ERR_SHAPE = 2,        /* bad sizes: B/H/N <= 0, H_q % H_kv != 0, bad cu_seqlens, ... */
-  SAGE2_ERR_UNSUPPORTED = 3,  /* head dim not 64/128, unknown dtype, non-finite sm_scale, ... */
+  SAGE2_ERR_UNSUPPORTED = 3,  /* head dim not a multiple of 8 in [8, 128], unknown dtype or flag, ... */
   SAGE2_ERR_ALIGN = 4,        /* pointer or stride not 16-byte aligned; workspace not 256-byte aligned */
   SAGE2_ERR_WORKSPACE = 5,    /* ws_bytes smaller than sage2_workspace_size() */
   SAGE2_ERR_HIP = 6           /* a kernel launch failed */
 } sage2_status;
 
 typedef enum { SAGE2_F16 = 0, SAGE2_BF16 = 1, SAGE2_F32 = 2 } sage2_dtype;
+
+/* Ablations of the method's smoothing steps (research record, "Three components"; visual companion,
+ * "Channel Outlier Smoothing"), for measuring what each one buys. 0 is the full method. */
+typedef enum {
+  SAGE2_NO_K_SMOOTH = 1,  /* quantize K without subtracting its channel means (k-bar = 0) */
+  SAGE2_NO_Q_SMOOTH = 2   /* quantize Q without its block means (q-bar = 0, so the correction is 0) */
+} sage2_flag;
 
 typedef struct {
   /* Sizes. Dense batch: B sequences of N_q queries and N_kv keys each.
@@ -77,6 +87,7 @@ typedef struct {
    * mode the tensors are packed [total_tokens, H, d] and the batch stride is ignored.
    * Strides times the element size must be multiples of 16 bytes. */
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  int32_t flags;  /* OR of sage2_flag values; 0 = the full method */
 } sage2_params;
 
 /* Byte offsets (from the workspace base) and byte sizes of the workspace buffers, for tests that

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libsage2.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
 F16, BF16, F32 = 0, 1, 2
+NO_K_SMOOTH, NO_Q_SMOOTH = 1, 2  # sage2_flag: ablations of the smoothing steps
 
 # Symbols the header declares; tests check that the library exports every one.
 EXPORTS = ("sage2_workspace_size", "sage2_quantize_smooth", "sage2_attn_fwd", "sage2_status_string",
@@ -38,6 +39,7 @@ class Params(ctypes.Structure):
         ("cu_seqlens_q_host", ctypes.c_void_p), ("cu_seqlens_kv_host", ctypes.c_void_p),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -112,10 +114,12 @@ def _stream_ptr(stream):
 
 def make_params(q, k, v, o=None, causal: bool = False, sm_scale: float = 0.0,
                 cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None, max_seqlen_kv=None,
-                out_dtype=None) -> Params:
+                out_dtype=None, flags: int = 0) -> Params:
     """Params for dense q [B, Nq, Hq, d], k/v [B, Nkv, Hkv, d] (any strides with channel stride 1),
-    or for packed q [Tq, Hq, d], k/v [Tkv, Hkv, d] with cu_seqlens (int32, B+1, device)."""
+    or for packed q [Tq, Hq, d], k/v [Tkv, Hkv, d] with cu_seqlens (int32, B+1, device).
+    `flags` takes NO_K_SMOOTH / NO_Q_SMOOTH (ablations; 0 = the full method)."""
     p = Params()
+    p.flags = int(flags)
     varlen = cu_seqlens_q is not None
     if varlen:
         if cu_seqlens_kv is None:
@@ -188,13 +192,13 @@ def debug_qk_i32(p: Params, ws, q_begin: int, q_count: int, s_out, stream=None):
 
 def attention(q, k, v, causal: bool = False, sm_scale: float = 0.0, out_dtype=None,
               cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None, max_seqlen_kv=None,
-              stream=None):
+              stream=None, flags: int = 0):
     """Allocates the output and a workspace with torch, then runs the pre-pass and the kernel."""
     import torch
     odt = out_dtype or q.dtype
     o = torch.empty(q.shape, dtype=odt, device=q.device)
     p = make_params(q, k, v, o, causal, sm_scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
-                    max_seqlen_kv)
+                    max_seqlen_kv, flags=flags)
     ws = torch.empty(workspace_size(p), dtype=torch.uint8, device=q.device)
     quantize_smooth(p, q, k, v, ws, stream)
     attn_fwd(p, ws, o, stream)

@@ -385,6 +385,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int c0 = 32 * cb + 8 * a4 + 4 * hh;
+      if (c0 >= a.dt) continue;  // zero padding of a smaller head dim (dt is a multiple of 8)
       const float4 sv = *reinterpret_cast<const float4*>(svp + c0);
       store4<OUT>(orow + ES * c0, o[cb][4 * a4] * sv.x * inv, o[cb][4 * a4 + 1] * sv.y * inv,
                   o[cb][4 * a4 + 2] * sv.z * inv, o[cb][4 * a4 + 3] * sv.w * inv);

@@ -40,7 +40,8 @@ sage2_status check_strides(const int64_t* s, int esize, bool varlen) {
 // Checks everything that does not involve a data pointer.
 sage2_status validate(const sage2_params* p) {
   if (!p) return SAGE2_ERR_NULL;
-  if (p->d != 64 && p->d != 128) return SAGE2_ERR_UNSUPPORTED;
+  if (p->d < 8 || p->d > 128 || p->d % 8) return SAGE2_ERR_UNSUPPORTED;
+  if (p->flags & ~(SAGE2_NO_K_SMOOTH | SAGE2_NO_Q_SMOOTH)) return SAGE2_ERR_UNSUPPORTED;
   if (p->in_dtype != SAGE2_F16 && p->in_dtype != SAGE2_BF16) return SAGE2_ERR_UNSUPPORTED;
   if (p->out_dtype != SAGE2_F16 && p->out_dtype != SAGE2_BF16 && p->out_dtype != SAGE2_F32)
     return SAGE2_ERR_UNSUPPORTED;
@@ -68,9 +69,12 @@ sage2_status validate(const sage2_params* p) {
   return SAGE2_OK;
 }
 
+// Head dim inside the workspace: the caller's d padded to 64 or 128.
+int padded_d(int d) { return d <= 64 ? 64 : 128; }
+
 void compute_layout(const sage2_params* p, sage2_ws_layout* L) {
   std::memset(L, 0, sizeof(*L));
-  const int64_t d = p->d;
+  const int64_t d = padded_d(p->d);
   for (int b = 0; b < p->B; ++b) {
     int64_t lq, lkv;
     seq_lengths(p, b, &lq, &lkv);
@@ -108,7 +112,10 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 void fill_args(const sage2_params* p, KArgs* a) {
   std::memset(a, 0, sizeof(*a));
-  a->B = p->B; a->Hq = p->H_q; a->Hkv = p->H_kv; a->Nq = p->N_q; a->Nkv = p->N_kv; a->d = p->d;
+  a->B = p->B; a->Hq = p->H_q; a->Hkv = p->H_kv; a->Nq = p->N_q; a->Nkv = p->N_kv;
+  a->d = padded_d(p->d);
+  a->dt = p->d;
+  a->flags = p->flags;
   a->causal = p->causal; a->in_dtype = p->in_dtype; a->out_dtype = p->out_dtype;
   a->varlen = varlen_of(p) ? 1 : 0;
   const float scale = p->sm_scale != 0.0f ? p->sm_scale : 1.0f / std::sqrt((float)p->d);
@@ -144,7 +151,7 @@ const char* sage2_status_string(sage2_status s) {
     case SAGE2_OK: return "ok";
     case SAGE2_ERR_NULL: return "a required pointer is NULL";
     case SAGE2_ERR_SHAPE: return "invalid sizes or sequence offsets";
-    case SAGE2_ERR_UNSUPPORTED: return "unsupported head dim, dtype, causal flag or scale";
+    case SAGE2_ERR_UNSUPPORTED: return "unsupported head dim, dtype, flag, causal flag or scale";
     case SAGE2_ERR_ALIGN: return "pointer or stride not aligned (16 bytes; workspace 256 bytes)";
     case SAGE2_ERR_WORKSPACE: return "workspace too small";
     case SAGE2_ERR_HIP: return "HIP kernel launch failed";

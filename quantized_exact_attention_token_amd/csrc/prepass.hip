@@ -77,11 +77,12 @@ __device__ inline void widen8(const uint4 v, float (&f)[8]) {
 
 // Rows [tok0, tok0 + n) of one head of a strided input, as 16-byte chunks for a block of 256
 // threads: chunk k of thread x is row (x + 256 k) / (D/8), channels 8 ((x + 256 k) % (D/8)) + [0, 8).
-// All of a thread's loads are issued before any is waited on; rows n..NROWS-1 are zero (they reread
-// row n-1, which exists whenever n > 0, and are then cleared).
+// All of a thread's loads are issued before any is waited on; rows n..NROWS-1 and channels dt..D-1
+// (the zero padding of a head dim below D) are zero: they reread row n-1 / the last real chunk,
+// which exist whenever n > 0, and are then cleared.
 template <int D, int NROWS>
 __device__ inline void load_rows(uint4 (&v)[NROWS * D / 8 / 256], const void* base, const int64_t* strides,
-                                 int b, int64_t tok0, int head, int n) {
+                                 int b, int64_t tok0, int head, int n, int dt) {
   constexpr int RW = D / 8;
   constexpr int IT = NROWS * RW / 256;
   static_assert(NROWS * RW % 256 == 0, "tile must split evenly over the block");
@@ -92,21 +93,24 @@ __device__ inline void load_rows(uint4 (&v)[NROWS * D / 8 / 256], const void* ba
     for (int k = 0; k < IT; ++k) {
       const int idx = threadIdx.x + 256 * k, r = idx / RW, ch = idx % RW;
       v[k] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) +
-                                             row_index(strides, b, tok0 + min(r, n - 1), head) + 8 * ch);
+                                             row_index(strides, b, tok0 + min(r, n - 1), head) +
+                                             8 * min(ch, dt / 8 - 1));
     }
 #pragma unroll
-    for (int k = 0; k < IT; ++k)
-      if ((threadIdx.x + 256 * k) / RW >= n) v[k] = make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < IT; ++k) {
+      const int idx = threadIdx.x + 256 * k;
+      if (idx / RW >= n || 8 * (idx % RW) >= dt) v[k] = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
 // The same rows, raw, into LDS rows of D elements.
 template <int D, int NROWS>
 __device__ inline void stage_rows(uint16_t (*dst)[D], const void* base, const int64_t* strides, int b,
-                                  int64_t tok0, int head, int n) {
+                                  int64_t tok0, int head, int n, int dt) {
   constexpr int RW = D / 8;
   uint4 v[NROWS * RW / 256];
-  load_rows<D, NROWS>(v, base, strides, b, tok0, head, n);
+  load_rows<D, NROWS>(v, base, strides, b, tok0, head, n, dt);
 #pragma unroll
   for (int k = 0; k < NROWS * RW / 256; ++k) {
     const int idx = threadIdx.x + 256 * k;
@@ -129,12 +133,12 @@ __global__ __launch_bounds__(256) void k_kstats(KArgs a) {
   const int j0 = u * kKVPad, n = min(kKVPad, s.kv_len - j0);
   __shared__ __attribute__((aligned(16))) uint16_t kr[kKVPad][D];
   __shared__ float vm[RPP][D];
-  stage_rows<D, kKVPad>(kr, a.k, a.ks, b, s.kv_start + j0, g, n);
+  stage_rows<D, kKVPad>(kr, a.k, a.ks, b, s.kv_start + j0, g, n, a.dt);
   {
     // V: this thread's chunks all share channels 8 (tid % RW) + [0, 8) (256 is a multiple of RW)
     const int ch = tid % RW, r0 = tid / RW;
     uint4 v[kKVPad * RW / 256];
-    load_rows<D, kKVPad>(v, a.v, a.vs, b, s.kv_start + j0, g, n);
+    load_rows<D, kKVPad>(v, a.v, a.vs, b, s.kv_start + j0, g, n, a.dt);
     float m8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < kKVPad * RW / 256; ++k) {
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256) void k_kreduce(KArgs a) {
     const int64_t out = ((int64_t)b * a.Hkv + g) * D + 32 * cg + tid;
     float kbar = 0.0f, sv = 0.0f, svinv = 0.0f;
     if (s.kv_len > 0) {
-      kbar = (float)(total / (double)s.kv_len);
+      kbar = (a.flags & SAGE2_NO_K_SMOOTH) ? 0.0f : (float)(total / (double)s.kv_len);
       if (amax != 0.0f) {
         sv = amax / 448.0f;     // V channel amax maps to 448, the largest e4m3 value
         svinv = 448.0f / amax;
@@ -278,13 +282,13 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
   const int i0 = qb * kQBlock, n = min(kQBlock, s.q_len - i0);
   __shared__ __attribute__((aligned(16))) uint16_t rows[kQBlock][D];
   __shared__ __attribute__((aligned(16))) float qbar[D];
-  stage_rows<D, kQBlock>(rows, a.q, a.qs, b, s.q_start + i0, h, n);
+  stage_rows<D, kQBlock>(rows, a.q, a.qs, b, s.q_start + i0, h, n, a.dt);
   __syncthreads();
   if (tid < D) {
     double sum = 0.0;
 #pragma unroll 16
     for (int i = 0; i < kQBlock; ++i) sum += (double)widen16<IN>(rows[i][tid]);
-    const float m = (float)(sum / (double)n);
+    const float m = (a.flags & SAGE2_NO_Q_SMOOTH) ? 0.0f : (float)(sum / (double)n);
     qbar[tid] = m;
     const int64_t at = ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + tid;
     ws_ptr<float>(a, a.lay.qbar)[at] = m;
@@ -355,13 +359,13 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
     svinv[tid] = ws_ptr<float>(a, a.lay.sv_inv)[sidx + tid];
   }
   const int n = max(0, min(kKVTile, s.kv_len - t * kKVTile));
-  stage_rows<D, kKVTile>(kr, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n);
+  stage_rows<D, kKVTile>(kr, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n, a.dt);
   __syncthreads();
   // V rows, scaled per channel (f32), into vt
   {
     constexpr int RW = D / 8;
     uint4 v[kKVTile * RW / 256];
-    load_rows<D, kKVTile>(v, a.v, a.vs, b, s.kv_start + t * kKVTile, g, n);
+    load_rows<D, kKVTile>(v, a.v, a.vs, b, s.kv_start + t * kKVTile, g, n, a.dt);
 #pragma unroll
     for (int k = 0; k < kKVTile * RW / 256; ++k) {
       const int idx = tid + 256 * k, key = idx / RW, ch = idx % RW;
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(256) void k_delta(KArgs a) {
     constexpr int RW = D / 8;
     const int n = max(0, min(kKVTile, s.kv_len - t * kKVTile));
     uint4 v[kKVTile * RW / 256];
-    load_rows<D, kKVTile>(v, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n);
+    load_rows<D, kKVTile>(v, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n, a.dt);
 #pragma unroll
     for (int k = 0; k < kKVTile * RW / 256; ++k) {
       const int idx = tid + 256 * k, key = idx / RW, ch = idx % RW;

@@ -18,7 +18,10 @@ enum SeqCol { kQStart = 0, kQLen, kKVStart, kKVLen, kQRow0, kKVRow0, kQBlk0, kDe
 
 // Everything a kernel needs, passed by value.
 struct KArgs {
-  int32_t B, Hq, Hkv, Nq, Nkv, d, causal, in_dtype, out_dtype, varlen;
+  int32_t B, Hq, Hkv, Nq, Nkv, causal, in_dtype, out_dtype, varlen;
+  int32_t d;      // head dim inside the workspace and kernels: 64 or 128
+  int32_t dt;     // the caller's head dim (a multiple of 8, <= d); channels dt..d-1 are zero
+  int32_t flags;  // sage2_flag bits
   float L;  // sm_scale * log2(e) in f32: logits are carried in base-2 units
   const void *q, *k, *v;
   void* o;

@@ -18,8 +18,10 @@ OUT_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32
 class GpuRun:
     """Inputs on the device, params, workspace, output."""
 
-    def __init__(self, w: W.Workload, out_dtype=None, layout: str = "bnhd", device="cuda"):
+    def __init__(self, w: W.Workload, out_dtype=None, layout: str = "bnhd", device="cuda",
+                 flags: int = 0):
         self.w = w
+        self.flags = flags
         q, k, v, cu = W.generate(w)
         self.q_cpu, self.k_cpu, self.v_cpu, self.cu_cpu = q, k, v, cu
         dev = torch.device(device)
@@ -32,7 +34,8 @@ class GpuRun:
         self.p = sage2.make_params(self.q, self.k, self.v, self.o, w.causal,
                                    cu_seqlens_q=self.cu, cu_seqlens_kv=self.cu,
                                    max_seqlen_q=w.Nq if cu is not None else None,
-                                   max_seqlen_kv=w.Nkv if cu is not None else None)
+                                   max_seqlen_kv=w.Nkv if cu is not None else None,
+                                   flags=flags)
         self.ws = torch.empty(sage2.workspace_size(self.p), dtype=torch.uint8, device=dev)
         self.lay = sage2.workspace_layout(self.p)
 
@@ -69,9 +72,11 @@ class GpuRun:
         return [(int(cu[i + 1] - cu[i]),) * 2 for i in range(len(cu) - 1)]
 
     def decode(self, ws: np.ndarray, b: int):
-        """Canonical pre-pass outputs of sequence b, shaped like the oracle's."""
+        """Canonical pre-pass outputs of sequence b, shaped like the oracle's (the head dim's zero
+        padding inside the workspace is checked and cut off)."""
         lay, w = self.lay, self.w
-        d, Hq, Hkv = w.d, w.Hq, w.Hkv
+        dt, Hq, Hkv = w.d, w.Hq, w.Hkv
+        d = 64 if dt <= 64 else 128  # head dim inside the workspace
         tab = ws[lay.seq_table:lay.seq_table + 4 * 8 * self.p.B].view(np.int32).reshape(-1, 8)
         qs, lq, ks, lk, qrow0, kvrow0, qblk0, delta0 = (int(x) for x in tab[b])
         nqb = (lq + 127) // 128
@@ -118,6 +123,11 @@ class GpuRun:
         out["v8"] = canon[:, :lk]
         dl = arr(lay.delta, np.float32, Hq * lay.delta_len).reshape(Hq, lay.delta_len)
         out["delta"] = dl[:, delta0:delta0 + nqb * kvpad].reshape(Hq, nqb, kvpad)[:, :, :lk]
+        if dt < d:
+            for name in ("kbar", "sv", "qbar", "qcode", "qcode_pad", "kcode", "v8"):
+                pad = out[name][..., dt:]
+                assert not pad.any(), f"{name}: head-dim padding channels are not zero"
+                out[name] = np.ascontiguousarray(out[name][..., :dt])
         return out
 
     def seq_inputs(self, b: int, heads=None):

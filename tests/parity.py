@@ -37,7 +37,7 @@ def check_sequence(run: H.GpuRun, b: int, heads=None, rows=None, ws=None, check_
         # no keys: every row is fully masked and outputs zeros
         assert np.all(run.out_seq(b)[h0:h0 + nh] == 0)
         return info
-    z = O.quantize(q, k, v, nthreads=nthreads)
+    z = O.quantize(q, k, v, flags=run.flags, nthreads=nthreads)
     qs, kvs = slice(h0, h0 + nh), slice(g0, g0 + ng)
     _eq("kbar", dec["kbar"][kvs], z.kbar)
     _eq("sv", dec["sv"][kvs], z.sv)

@@ -60,9 +60,12 @@ def test_workspace_size_closed_form(lib):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("d", 96, sage2.ERR_UNSUPPORTED),
+    ("d", 100, sage2.ERR_UNSUPPORTED),   # not a multiple of 8
+    ("d", 136, sage2.ERR_UNSUPPORTED),
     ("d", 256, sage2.ERR_UNSUPPORTED),
     ("d", 0, sage2.ERR_UNSUPPORTED),
+    ("flags", 4, sage2.ERR_UNSUPPORTED),
+    ("flags", -1, sage2.ERR_UNSUPPORTED),
     ("in_dtype", sage2.F32, sage2.ERR_UNSUPPORTED),
     ("out_dtype", 7, sage2.ERR_UNSUPPORTED),
     ("causal", 2, sage2.ERR_UNSUPPORTED),
@@ -76,6 +79,26 @@ def test_workspace_size_closed_form(lib):
 ])
 def test_rejects_bad_sizes(lib, field, value, status):
     assert _ws_status(lib, _params(**{field: value}))[0] == status
+
+
+@pytest.mark.parametrize("d,padded", [(8, 64), (48, 64), (64, 64), (72, 128), (96, 128), (128, 128)])
+def test_head_dim_padding_layout(lib, d, padded):
+    """Any multiple of 8 up to 128 is accepted; the workspace is that of the padded head dim."""
+    def mk(dd):
+        p = _params(d=dd)
+        for name in ("q_stride", "o_stride"):
+            getattr(p, name)[:] = (300 * 8 * dd, 8 * dd, dd)
+        for name in ("k_stride", "v_stride"):
+            getattr(p, name)[:] = (500 * 2 * dd, 2 * dd, dd)
+        return p
+    st, n = _ws_status(lib, mk(d))
+    assert st == sage2.OK
+    assert n == _ws_status(lib, mk(padded))[1]
+
+
+def test_ablation_flags_accepted(lib):
+    for f in (0, sage2.NO_K_SMOOTH, sage2.NO_Q_SMOOTH, sage2.NO_K_SMOOTH | sage2.NO_Q_SMOOTH):
+        assert _ws_status(lib, _params(flags=f))[0] == sage2.OK
 
 
 def test_rejects_misaligned_strides(lib):

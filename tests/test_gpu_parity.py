@@ -22,8 +22,8 @@ def _report(name, info):
                                          for k, v in info.items()), flush=True)
 
 
-def _full_check(w, out_dtype=None, layout="bnhd"):
-    run = H.GpuRun(w, out_dtype=out_dtype, layout=layout)
+def _full_check(w, out_dtype=None, layout="bnhd", flags=0):
+    run = H.GpuRun(w, out_dtype=out_dtype, layout=layout, flags=flags)
     run.run()
     ws = run.ws_host()
     for b, _ in enumerate(run.sequences()):
@@ -110,4 +110,33 @@ def test_rising_row_max_renormalizes(case):
     x = O.logits(z, causal, rows=np.array([511], np.int32))[:, 0]
     span = float((x.max(axis=-1) - x.min(axis=-1)).min())
     assert span > 3 * 64, f"logit span {span} too small to reach the renormalization"
+
+
+HEAD_DIMS = [
+    # (d, dtype, causal, Hq, Hkv): padded to 64 or 128 inside the workspace
+    (8, torch.float16, False, 2, 2),
+    (48, torch.float16, False, 4, 2),
+    (80, torch.bfloat16, False, 4, 1),
+    (96, torch.bfloat16, True, 4, 2),
+    (120, torch.float16, True, 2, 2),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_DIMS, ids=lambda c: "d%d_%s_%s" % (
+    c[0], str(c[1]).split(".")[-1], "causal" if c[2] else "full"))
+def test_head_dim_padding(case):
+    """Head dims below 64/128: zero channels inside the workspace (checked by the decoder), the same
+    codes, scales, correction and output as the oracle run on the true head dim, and the default
+    softmax scale taken from the true d."""
+    d, dt, causal, hq, hkv = case
+    _full_check(W.custom(1, hq, hkv, 200, 200, d, dt, causal, seed=300 + d))
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3], ids=["no_k_smooth", "no_q_smooth", "no_smoothing"])
+def test_smoothing_ablations(flags):
+    """The ablation flags reproduce the oracle's ablations bit for bit (codes, scales, correction)
+    and to the usual bar on the output; accuracy against FP64 is reported by the parity check."""
+    w = W.custom(1, 4, 2, 300, 300, 128, torch.bfloat16, True, seed=77, k_offset_std=4.0,
+                 q_offset_std=4.0)
+    _full_check(w, flags=flags)
 
