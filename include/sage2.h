@@ -57,11 +57,15 @@ typedef enum {
 
 typedef enum { SAGE2_F16 = 0, SAGE2_BF16 = 1, SAGE2_F32 = 2 } sage2_dtype;
 
-/* Ablations of the method's smoothing steps (research record, "Three components"; visual companion,
- * "Channel Outlier Smoothing"), for measuring what each one buys. 0 is the full method. */
+/* Ablations of the method's smoothing and scale granularity (research record, "Three components";
+ * visual companion, "Channel Outlier Smoothing" and "Per-Thread INT4 Geometry"), for measuring what
+ * each one buys. 0 is the full method. */
 typedef enum {
-  SAGE2_NO_K_SMOOTH = 1,  /* quantize K without subtracting its channel means (k-bar = 0) */
-  SAGE2_NO_Q_SMOOTH = 2   /* quantize Q without its block means (q-bar = 0, so the correction is 0) */
+  SAGE2_NO_K_SMOOTH = 1,      /* quantize K without subtracting its channel means (k-bar = 0) */
+  SAGE2_NO_Q_SMOOTH = 2,      /* quantize Q without its block means (q-bar = 0, so the correction is 0) */
+  SAGE2_PER_BLOCK_SCALES = 4  /* one INT4 scale per 128-token Q block and per 64-key K block instead of
+                               * the per-thread groups (section "Per-Thread INT4 Geometry" contrasts
+                               * the two); the attention kernel is unchanged */
 } sage2_flag;
 
 typedef struct {

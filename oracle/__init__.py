@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "libsage2_oracle.so")
 
 NO_K_SMOOTH = 1
 NO_Q_SMOOTH = 2
+PER_BLOCK = 4
 ATTN_NO_P8 = 1
 
 _lib = None

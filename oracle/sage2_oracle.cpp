@@ -132,6 +132,9 @@ extern "C" {
 enum {
   ORC_NO_K_SMOOTH = 1,  // ablation: skip the K mean subtraction
   ORC_NO_Q_SMOOTH = 2,  // ablation: skip the Q block mean subtraction (and so the correction term)
+  ORC_PER_BLOCK = 4,    // ablation: per-block scales (one per 128-token Q block, one per 64-key K
+                        // block) in place of the per-thread ones ([VIZ] Per-Thread INT4 Geometry
+                        // contrasts the two)
 };
 enum {
   ORC_ATTN_NO_P8 = 1,   // keep P~ unquantized (used to compare the online form with a two-pass form)
@@ -184,7 +187,21 @@ int orc_quantize(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int fl
         KT[(size_t)j * d + c] = K[(size_t)j * d + c] - kbar[(size_t)g * d + c];
     // 3. K codes: one scale per group of 16 keys (kgroup), shared by all channels.
     //    A group's keys all lie in one 32-key tile, so only that tile is scanned for members.
-    for (int grp = 0; grp < ngk; ++grp) {
+    //    Per-block ablation: one scale per 64-key block (its four groups share it).
+    if (flags & ORC_PER_BLOCK) {
+      for (int j0 = 0; j0 < Lkv; j0 += 64) {
+        const int j1 = std::min(Lkv, j0 + 64);
+        float amax = 0.0f;
+        for (int j = j0; j < j1; ++j)
+          for (int c = 0; c < d; ++c) amax = std::max(amax, std::fabs(KT[(size_t)j * d + c]));
+        const Int4Scale s = int4_scale(amax);
+        for (int grp = j0 / 16; grp < std::min(ngk, j0 / 16 + 4); ++grp) sk[(size_t)g * ngk + grp] = s.s;
+        for (int j = j0; j < j1; ++j)
+          for (int c = 0; c < d; ++c)
+            kcode[((size_t)g * Lkv + j) * d + c] = int4_code(KT[(size_t)j * d + c], s.inv);
+      }
+    }
+    for (int grp = 0; grp < ngk && !(flags & ORC_PER_BLOCK); ++grp) {
       const int j0 = 32 * (grp / 2), j1 = std::min(Lkv, j0 + 32);
       float amax = 0.0f;
       for (int j = j0; j < j1; ++j)
@@ -228,12 +245,18 @@ int orc_quantize(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int fl
         qb[c] = (flags & ORC_NO_Q_SMOOTH) ? 0.0f : (float)(sum / (double)(i1 - i0));
       }
       // 3. Q codes: one scale per token (a lane owns one query column of S^T on gfx950).
+      //    Per-block ablation: one scale for the whole 128-token block.
+      float bmax = 0.0f;
+      if (flags & ORC_PER_BLOCK)
+        for (int i = i0; i < i1; ++i)
+          for (int c = 0; c < d; ++c) bmax = std::max(bmax, std::fabs(Q[(size_t)i * d + c] - qb[c]));
       for (int i = i0; i < i1; ++i) {
         float amax = 0.0f;
         for (int c = 0; c < d; ++c) {
           qt[c] = Q[(size_t)i * d + c] - qb[c];
           amax = std::max(amax, std::fabs(qt[c]));
         }
+        if (flags & ORC_PER_BLOCK) amax = bmax;
         const Int4Scale s = int4_scale(amax);
         sq[(size_t)h * Lq + i] = s.s;
         for (int c = 0; c < d; ++c) qcode[((size_t)h * Lq + i) * d + c] = int4_code(qt[c], s.inv);

@@ -302,6 +302,28 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
   float qm[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) qm[e] = qbar[CPL * li + e];
+  // per-block ablation: one scale for the whole block (the largest |q - qbar| in it)
+  const bool per_block = a.flags & SAGE2_PER_BLOCK_SCALES;
+  float bmax = 0.0f;
+  if (per_block) {
+    __shared__ float wmax[4];
+    for (int it = 0; it < 8; ++it) {
+      const int r = 32 * wave + 4 * it + (lane >> 4);
+      float raw[8];
+      if constexpr (CPL == 8) {
+        widen8<IN>(*reinterpret_cast<const uint4*>(&rows[r][8 * li]), raw);
+      } else {
+        const uint2 v2 = *reinterpret_cast<const uint2*>(&rows[r][4 * li]);
+        widen8<IN>(make_uint4(v2.x, v2.y, 0, 0), raw);
+      }
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) bmax = fmaxf(bmax, r < n ? fabsf(raw[e] - qm[e]) : 0.0f);
+    }
+    bmax = wave_max(bmax);
+    if (lane == 0) wmax[wave] = bmax;
+    __syncthreads();
+    bmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  }
 #pragma unroll 2
   for (int it = 0; it < 8; ++it) {
     const int r = 32 * wave + 4 * it + (lane >> 4);  // 4 rows per wave at a time, 16 lanes each
@@ -321,9 +343,9 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
       qt[e] = r < n ? raw[e] - qm[e] : 0.0f;
       amax = fmaxf(amax, fabsf(qt[e]));
     }
-    amax = max16(amax);
+    amax = per_block ? bmax : max16(amax);
     const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
-    const float scale = amax == 0.0f ? 0.0f : amax / 7.0f;
+    const float scale = amax == 0.0f || r >= n ? 0.0f : amax / 7.0f;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) code[e] = int4_code(qt[e], inv);
     store_row_fp6_16<D>(reinterpret_cast<uint32_t*>(qcode + prow * (3 * D / 4)), code, li);
@@ -401,6 +423,13 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
       }
     }
     amax = wave_max(amax);
+    if (a.flags & SAGE2_PER_BLOCK_SCALES) {
+      // per-block ablation: one scale for the 64-key tile (the four groups' largest)
+      __shared__ float gmax[4];
+      if (lane == 0) gmax[wave] = amax;
+      __syncthreads();
+      amax = fmaxf(fmaxf(gmax[0], gmax[1]), fmaxf(gmax[2], gmax[3]));
+    }
     const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
     const float scale = amax == 0.0f ? 0.0f : amax / 7.0f;
     uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode);

@@ -132,7 +132,8 @@ def test_head_dim_padding(case):
     _full_check(W.custom(1, hq, hkv, 200, 200, d, dt, causal, seed=300 + d))
 
 
-@pytest.mark.parametrize("flags", [1, 2, 3], ids=["no_k_smooth", "no_q_smooth", "no_smoothing"])
+@pytest.mark.parametrize("flags", [1, 2, 3, 4, 7], ids=["no_k_smooth", "no_q_smooth", "no_smoothing",
+                                                       "per_block_scales", "naive_per_block"])
 def test_smoothing_ablations(flags):
     """The ablation flags reproduce the oracle's ablations bit for bit (codes, scales, correction)
     and to the usual bar on the output; accuracy against FP64 is reported by the parity check."""

@@ -501,3 +501,38 @@ def test_q_smoothing_matters_with_q_offset():
     konly, _ = O.attn_quant(O.quantize(q, k, v, flags=O.NO_Q_SMOOTH), False)
     assert np.abs(full - exact).max() < np.abs(konly - exact).max()
     assert _cos(full, exact) > 0.99
+
+
+def test_per_block_scales_are_block_maxima():
+    """Per-block ablation ([VIZ: Per-Thread INT4 Geometry] contrasts per-block and per-thread
+    scales): each 128-token Q block's scale is the largest per-token scale in it, each 64-key K
+    block's scale the largest of its four 16-key group scales (amax/7 is monotone in amax and
+    correctly rounded), and every code still round-trips within half its scale."""
+    w = W.custom(1, 2, 1, 300, 200, 64, torch.float16, seed=21)
+    q, k, v = _seq(w)
+    zt = O.quantize(q, k, v)
+    zb = O.quantize(q, k, v, flags=O.PER_BLOCK)
+    for b0 in range(0, 300, 128):
+        blk = slice(b0, min(300, b0 + 128))
+        assert np.all(zb.sq[:, blk] == zt.sq[:, blk].max(axis=1, keepdims=True))
+    ngk = zt.sk.shape[1]
+    for g0 in range(0, ngk, 4):
+        grp = slice(g0, min(ngk, g0 + 4))
+        assert np.all(zb.sk[:, grp] == zt.sk[:, grp].max(axis=1, keepdims=True))
+    # round trip within half a scale, for both operands
+    qt = q - np.repeat(zb.qbar, 128, axis=1)[:, :300]
+    assert np.all(np.abs(zb.qcode * zb.sq[..., None] - qt) <= zb.sq[..., None] / 2 * (1 + 1e-6))
+    kt = k - zb.kbar[:, None, :]
+    sk_key = zb.sk[:, [O.kgroup(j) for j in range(200)]]
+    assert np.all(np.abs(zb.kcode * sk_key[..., None] - kt) <= sk_key[..., None] / 2 * (1 + 1e-6))
+    assert np.array_equal(zb.v8, zt.v8) and np.array_equal(zb.delta, zt.delta)
+
+
+def test_per_thread_scales_beat_per_block_on_outliers():
+    """The pages' claim that thread-granularity scales recover accuracy lost by coarser ones."""
+    w = W.WORKLOADS["tiny"]
+    q, k, v = _seq(w)
+    exact = O.attn_fp64(q, k, v, False)
+    per_thread, _ = O.attn_quant(O.quantize(q, k, v), False)
+    per_block, _ = O.attn_quant(O.quantize(q, k, v, flags=O.PER_BLOCK), False)
+    assert _cos(per_thread, exact) > _cos(per_block, exact)
