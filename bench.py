@@ -97,6 +97,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: time sage2_attn_fwd on the d=128 length "
+                         "sweep (N = 4K..32K, causal and not) and print one JSON line with a row "
+                         "per configuration")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel whose HBM counters scale the attention kernel's)")
@@ -122,6 +126,38 @@ def main():
             torch.mul(src, 1, out=dst)  # an elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.sweep:
+        rows = []
+        for name, w in W.SWEEP.items():
+            run = H.GpuRun(w)
+            run.prepass()
+            for _ in range(max(1, args.warmup)):
+                run.attn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            stream = torch.cuda.current_stream()
+            pre = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            pre[0].record(stream)
+            run.prepass()
+            pre[1].record(stream)
+            for a, b in evs:
+                a.record(stream)
+                run.attn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in evs)
+            avg = sum(ms) / len(ms)
+            ops = w.attention_ops()
+            rows.append({"workload": name, "N": w.Nq, "causal": w.causal, "attn_ms": avg,
+                         "attn_ms_min": ms[0], "kernel_tops": ops / (avg * 1e-3) / 1e12,
+                         "frac_of_peak": ops / (avg * 1e-3) / 1e12 / PEAK_TOPS,
+                         "prepass_ms": pre[0].elapsed_time(pre[1])})
+            print(f"[sweep] {name}: {rows[-1]['kernel_tops']:.0f} TOPS", file=sys.stderr, flush=True)
+            del run
+            torch.cuda.empty_cache()
+        print(json.dumps({"metric": METRIC, "unit": "TOPS", "config": "B1 H32 d128 bf16",
+                          "steps": args.steps, "sweep": rows}), flush=True)
         return
     w = (W.WORKLOADS | W.SWEEP)[args.workload]
     run = H.GpuRun(w)
