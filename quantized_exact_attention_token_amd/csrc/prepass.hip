@@ -214,65 +214,60 @@ __global__ __launch_bounds__(256) void k_kreduce(KArgs a) {
   }
 }
 
-// INT4 code of x given the group's inverse scale: round to nearest even, clamp to [-7, 7].
-__device__ inline int int4_code(float x, float inv) {
-  const float y = x * inv;
-  return (int)fminf(7.0f, fmaxf(-7.0f, rintf(y)));
+// INT4 code of x given its group's inverse scale, as an exact small-integer float: round to nearest
+// even, clamp to [-7, 7] (never active: |x| <= amax and inv = 7/amax rounded keep |x * inv| < 7.5),
+// and + 0 so that a code 0 is +0 (no negative-zero field below).
+__device__ inline float int4_codef(float x, float inv) {
+  return __builtin_amdgcn_fmed3f(rintf(x * inv), -7.0f, 7.0f) + 0.0f;
 }
 
-// e2m3 (FP6) encoding of an INT4 code: every integer in [-7, 7] is exact in e2m3 (1 sign,
-// 2 exponent, 3 mantissa bits; magnitudes 1 2 3 4 5 6 7 = 001000 010000 010100 011000 011010
-// 011100 011110). The attention kernel feeds these fields to the fp6 MFMA, whose f32 accumulation
-// of such small integer products is exact.
-__device__ inline uint32_t e2m3_of_int4(int c) {
-  const int m = c < 0 ? -c : c;
-  const uint32_t mag = (uint32_t)(0x1E1C1A1814100800ull >> (8 * m)) & 0x3Fu;
-  return mag | (c < 0 ? 0x20u : 0u);
-}
+typedef float v16f_t __attribute__((ext_vector_type(16)));
 
-// Writes one row of D INT4 codes as packed e2m3 fields: channel ch occupies bits [6 ch, 6 ch + 6)
-// of the row, little-endian across dwords (3D/16 dwords).
-// Row-parallel form: 16 lanes per row, lane li holding channels [CPL*li, CPL*li + CPL) (CPL =
-// D/16). Leaders of groups of GL = 96/(6 CPL) lanes assemble their group's 96 bits from the
-// neighbours' fields and write them as three dwords: no block barrier.
-template <int D>
-__device__ inline void store_row_fp6_16(uint32_t* row, const int (&code)[D / 16], int li) {
-  constexpr int CPL = D / 16;
-  uint64_t v = 0;
+// 32 INT4 codes of consecutive channels (exact integers in float) -> 6 dwords of e2m3 (FP6) fields,
+// field i (channel i) at bits [6i, 6i + 6), little-endian across the dwords: the fp6 MFMA operand
+// format. Every integer in [-7, 7] is exact in e2m3, so the conversion is exact; the attention
+// kernel feeds these fields to the fp6 MFMA, whose f32 accumulation of such integer products is
+// exact. v_cvt_scalef32_2xpk16_fp6_f32 (scale 1) takes field 2i from element i of its first source
+// and field 2i + 1 from element i of its second (checked bit for bit against a software packing).
+__device__ inline void store_fp6_32(uint8_t* dst, const float (&c)[32]) {
+  v16f_t ev, od;
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) v |= (uint64_t)e2m3_of_int4(code[e]) << (6 * e);
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  if constexpr (CPL == 8) {  // 48 bits per lane, pairs of lanes make 3 dwords
-    const uint32_t nlo = __shfl_down(lo, 1, 16), nhi = __shfl_down(hi, 1, 16);
-    if ((li & 1) == 0) {
-      uint32_t* dst = row + 3 * (li >> 1);
-      dst[0] = lo;
-      dst[1] = (hi & 0xFFFFu) | (nlo << 16);
-      dst[2] = (nlo >> 16) | (nhi << 16);
-    }
-  } else {  // CPL == 4: 24 bits per lane, quads of lanes make 3 dwords
-    const uint32_t b = __shfl_down(lo, 1, 16), c = __shfl_down(lo, 2, 16), d = __shfl_down(lo, 3, 16);
-    if ((li & 3) == 0) {
-      uint32_t* dst = row + 3 * (li >> 2);
-      dst[0] = lo | (b << 24);
-      dst[1] = (b >> 8) | (c << 16);
-      dst[2] = (c >> 16) | (d << 8);
-    }
+  for (int i = 0; i < 16; ++i) {
+    ev[i] = c[2 * i];
+    od[i] = c[2 * i + 1];
   }
+  const auto w = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  *reinterpret_cast<uint2*>(dst + 8) = make_uint2(w[2], w[3]);
+  *reinterpret_cast<uint2*>(dst + 16) = make_uint2(w[4], w[5]);
 }
 
-__device__ inline float max16(float x) {
+// max over the lanes of an aligned group of LPR lanes (LPR a power of two <= 64)
+template <int LPR>
+__device__ inline float group_max(float x) {
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 16));
+  for (int o = LPR / 2; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
   return x;
+}
+
+// The 32 raw elements [c0, c0 + 32) of a staged LDS row, widened.
+template <int IN>
+__device__ inline void widen32(const uint16_t* p, float (&f)[32]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float g[8];
+    widen8<IN>(*reinterpret_cast<const uint4*>(p + 8 * k), g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[8 * k + e] = g[e];
+  }
 }
 
 // ---- Q: block mean, per-token INT4 codes -------------------------------------------------------
 // grid (Q blocks, H_q, B), block 256. The block's rows are read once, coalesced, into LDS (rows past
 // the sequence end are zero and add +0.0 to the fp64 sums); thread c sums channel c in row order.
-// Each of the 4 waves then quantizes every 4th row, 16 lanes per row with 8 channels each (one scale
-// per token: on gfx950 a lane owns one query column of the S^T = K Q^T MFMA tile, so the
-// per-thread group is one token).
+// The rows are then quantized with D/32 lanes per row and 32 channels per lane (one scale per
+// token: on gfx950 a lane owns one query column of the S^T = K Q^T MFMA tile, so the per-thread
+// group is one token).
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -297,59 +292,48 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
   __syncthreads();
   uint8_t* qcode = ws_ptr<uint8_t>(a, a.lay.qcode);
   float* sq = ws_ptr<float>(a, a.lay.sq);
-  constexpr int CPL = D / 16;  // channels per lane: 8 (D = 128) or 4 (D = 64)
-  const int li = lane & 15;
-  float qm[CPL];
+  // LPR lanes per row, 32 channels each: rows [r0, r0 + 256 / LPR) per pass of the block
+  constexpr int LPR = D / 32;
+  constexpr int RPP = 256 / LPR;
+  const int lr = lane % LPR, c0 = 32 * lr;
+  float qm[32];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) qm[e] = qbar[CPL * li + e];
+  for (int e = 0; e < 32; ++e) qm[e] = qbar[c0 + e];
   // per-block ablation: one scale for the whole block (the largest |q - qbar| in it)
   const bool per_block = a.flags & SAGE2_PER_BLOCK_SCALES;
   float bmax = 0.0f;
   if (per_block) {
     __shared__ float wmax[4];
-    for (int it = 0; it < 8; ++it) {
-      const int r = 32 * wave + 4 * it + (lane >> 4);
-      float raw[8];
-      if constexpr (CPL == 8) {
-        widen8<IN>(*reinterpret_cast<const uint4*>(&rows[r][8 * li]), raw);
-      } else {
-        const uint2 v2 = *reinterpret_cast<const uint2*>(&rows[r][4 * li]);
-        widen8<IN>(make_uint4(v2.x, v2.y, 0, 0), raw);
-      }
+    for (int r0 = 0; r0 < kQBlock; r0 += RPP) {
+      const int r = r0 + tid / LPR;
+      float raw[32];
+      widen32<IN>(&rows[r][c0], raw);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) bmax = fmaxf(bmax, r < n ? fabsf(raw[e] - qm[e]) : 0.0f);
+      for (int e = 0; e < 32; ++e) bmax = fmaxf(bmax, r < n ? fabsf(raw[e] - qm[e]) : 0.0f);
     }
     bmax = wave_max(bmax);
     if (lane == 0) wmax[wave] = bmax;
     __syncthreads();
     bmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   }
-#pragma unroll 2
-  for (int it = 0; it < 8; ++it) {
-    const int r = 32 * wave + 4 * it + (lane >> 4);  // 4 rows per wave at a time, 16 lanes each
+  for (int r0 = 0; r0 < kQBlock; r0 += RPP) {
+    const int r = r0 + tid / LPR;
     const int64_t prow = (int64_t)h * a.lay.q_rows + s.q_row0 + i0 + r;
-    float raw[8];
-    if constexpr (CPL == 8) {
-      widen8<IN>(*reinterpret_cast<const uint4*>(&rows[r][8 * li]), raw);
-    } else {
-      const uint2 v2 = *reinterpret_cast<const uint2*>(&rows[r][4 * li]);
-      widen8<IN>(make_uint4(v2.x, v2.y, 0, 0), raw);
-    }
-    int code[CPL];
-    float qt[CPL];
+    float qt[32];
+    widen32<IN>(&rows[r][c0], qt);
     float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      qt[e] = r < n ? raw[e] - qm[e] : 0.0f;
+    for (int e = 0; e < 32; ++e) {
+      qt[e] = r < n ? qt[e] - qm[e] : 0.0f;
       amax = fmaxf(amax, fabsf(qt[e]));
     }
-    amax = per_block ? bmax : max16(amax);
+    amax = per_block ? bmax : group_max<LPR>(amax);
     const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
     const float scale = amax == 0.0f || r >= n ? 0.0f : amax / 7.0f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) code[e] = int4_code(qt[e], inv);
-    store_row_fp6_16<D>(reinterpret_cast<uint32_t*>(qcode + prow * (3 * D / 4)), code, li);
-    if (li == 0) sq[prow] = scale;
+    for (int e = 0; e < 32; ++e) qt[e] = int4_codef(qt[e], inv);
+    store_fp6_32(qcode + prow * (3 * D / 4) + 24 * lr, qt);
+    if (lr == 0) sq[prow] = scale;
   }
 }
 
@@ -360,12 +344,11 @@ __device__ inline int tile_key(int h, int s) { return 32 * (s >> 4) + 8 * ((s & 
 // ---- K: per-16-key-group INT4 codes; V: FP8 codes in the attention kernel's tile layout -------
 // grid (64-key tiles, H_kv, B), block 256. The tile's K and V rows are staged in LDS with 16-byte
 // loads (zero past the sequence end). Wave w quantizes K group w of the tile: the 16 keys of
-// 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half owns), 4 keys at a
-// time with 16 lanes per key; the smoothed values stay in registers between the group max and the
-// codes.
+// 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half owns), D/32 lanes
+// per key with 32 channels each; the smoothed values stay in registers between the group max and
+// the codes.
 template <int D, int IN>
 __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
-  constexpr int CPL = D / 16;  // channels per lane in a 16-lane key row
   const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seq s = load_seq(a, b);
@@ -397,30 +380,21 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
       for (int e = 0; e < 8; ++e) vt[key][8 * ch + e] = f[e] * svinv[8 * ch + e];
     }
   }
-  // K group of this wave
+  // K group of this wave: its 16 keys, LPR lanes per key with 32 channels each (for D = 64 the
+  // upper half-wave repeats the lower one and does not store)
   {
-    const int half = wave & 1, sub = wave >> 1, li = lane & 15;
-    float km[CPL];
-#pragma unroll
-    for (int x = 0; x < CPL; ++x) km[x] = kbar[CPL * li + x];
-    float val[4][CPL];
+    constexpr int LPR = D / 32;
+    const int half = wave & 1, sub = wave >> 1;
+    const int lr = lane % LPR, c0 = 32 * lr;
+    const int e = (lane / LPR) & 15;
+    const int key = 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);  // within the tile
+    float val[32];
+    widen32<IN>(&kr[key][c0], val);
     float amax = 0.0f;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int e = 4 * it + (lane >> 4);
-      const int key = 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);  // within the tile
-      float raw[8];
-      if constexpr (CPL == 8) {
-        widen8<IN>(*reinterpret_cast<const uint4*>(&kr[key][8 * li]), raw);
-      } else {
-        const uint2 v2 = *reinterpret_cast<const uint2*>(&kr[key][4 * li]);
-        widen8<IN>(make_uint4(v2.x, v2.y, 0, 0), raw);
-      }
-#pragma unroll
-      for (int x = 0; x < CPL; ++x) {
-        val[it][x] = key < n ? raw[x] - km[x] : 0.0f;
-        amax = fmaxf(amax, fabsf(val[it][x]));
-      }
+    for (int x = 0; x < 32; ++x) {
+      val[x] = key < n ? val[x] - kbar[c0 + x] : 0.0f;
+      amax = fmaxf(amax, fabsf(val[x]));
     }
     amax = wave_max(amax);
     if (a.flags & SAGE2_PER_BLOCK_SCALES) {
@@ -432,17 +406,12 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
     }
     const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
     const float scale = amax == 0.0f ? 0.0f : amax / 7.0f;
-    uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int e = 4 * it + (lane >> 4);
-      const int j = t * kKVTile + 32 * sub + 8 * (e >> 2) + 4 * half + (e & 3);
-      int code[CPL];
-#pragma unroll
-      for (int x = 0; x < CPL; ++x) code[x] = int4_code(val[it][x], inv);
-      store_row_fp6_16<D>(reinterpret_cast<uint32_t*>(kcode + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (3 * D / 4)),
-                          code, li);
-    }
+    for (int x = 0; x < 32; ++x) val[x] = int4_codef(val[x], inv);
+    const int j = t * kKVTile + key;
+    if (lane < 16 * LPR)
+      store_fp6_32(ws_ptr<uint8_t>(a, a.lay.kcode) + ((int64_t)g * a.lay.kv_rows + s.kv_row0 + j) * (3 * D / 4) + 24 * lr,
+                   val);
     if (lane == 0)
       ws_ptr<float>(a, a.lay.sk)[(int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16 + 4 * t + wave] = scale;
   }
