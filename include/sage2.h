@@ -63,9 +63,14 @@ typedef enum { SAGE2_F16 = 0, SAGE2_BF16 = 1, SAGE2_F32 = 2 } sage2_dtype;
 typedef enum {
   SAGE2_NO_K_SMOOTH = 1,      /* quantize K without subtracting its channel means (k-bar = 0) */
   SAGE2_NO_Q_SMOOTH = 2,      /* quantize Q without its block means (q-bar = 0, so the correction is 0) */
-  SAGE2_PER_BLOCK_SCALES = 4  /* one INT4 scale per 128-token Q block and per 64-key K block instead of
+  SAGE2_PER_BLOCK_SCALES = 4, /* one INT4 scale per 128-token Q block and per 64-key K block instead of
                                * the per-thread groups (section "Per-Thread INT4 Geometry" contrasts
                                * the two); the attention kernel is unchanged */
+  SAGE2_NO_FP32_FOLD = 8      /* single-level P~V accumulation: the output accumulates across key tiles
+                               * inside the FP8 MFMA instead of being folded into FP32 once per tile
+                               * (research record, "Three components": FP8 accumulation loses
+                               * accuracy). Its result depends on the MFMA's inexact accumulation and
+                               * is not reproduced by the CPU oracle */
 } sage2_flag;
 
 typedef struct {

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libsage2.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)
 F16, BF16, F32 = 0, 1, 2
-NO_K_SMOOTH, NO_Q_SMOOTH, PER_BLOCK_SCALES = 1, 2, 4  # sage2_flag: ablations
+NO_K_SMOOTH, NO_Q_SMOOTH, PER_BLOCK_SCALES, NO_FP32_FOLD = 1, 2, 4, 8  # sage2_flag: ablations
 
 # Symbols the header declares; tests check that the library exports every one.
 EXPORTS = ("sage2_workspace_size", "sage2_quantize_smooth", "sage2_attn_fwd", "sage2_status_string",
@@ -117,7 +117,8 @@ def make_params(q, k, v, o=None, causal: bool = False, sm_scale: float = 0.0,
                 out_dtype=None, flags: int = 0) -> Params:
     """Params for dense q [B, Nq, Hq, d], k/v [B, Nkv, Hkv, d] (any strides with channel stride 1),
     or for packed q [Tq, Hq, d], k/v [Tkv, Hkv, d] with cu_seqlens (int32, B+1, device).
-    `flags` takes NO_K_SMOOTH / NO_Q_SMOOTH / PER_BLOCK_SCALES (ablations; 0 = the full method)."""
+    `flags` takes NO_K_SMOOTH / NO_Q_SMOOTH / PER_BLOCK_SCALES / NO_FP32_FOLD (ablations; 0 = the
+    full method)."""
     p = Params()
     p.flags = int(flags)
     varlen = cu_seqlens_q is not None

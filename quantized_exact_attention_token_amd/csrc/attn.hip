@@ -197,7 +197,10 @@ __device__ inline v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
 // One workgroup = one (sequence, q head, 128-query block); 4 waves x 32 queries. K/V tiles of 128
 // keys are staged once per workgroup in LDS (double-buffered, next tile's global loads in flight
 // while the current tile is computed).
-template <int D, int CAUSAL, int OUT>
+// NOFOLD = 1 is the ablation without the two-level accumulation: the output accumulates across
+// tiles inside the FP8 MFMA (rescaled by alpha in registers each tile), which on gfx950 adds its C
+// input with less than FP32 precision.
+template <int D, int CAUSAL, int OUT, int NOFOLD>
 __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   constexpr int NC6 = D / 64;   // fp6 MFMAs per 32-key subtile (64 channels each)
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
       // the output frame starts at the first tile with a visible key; renormalize (rarely) before
       // the fold factor 2^(mb - ref) could leave the f32 range
       if (m == kNegInf) ref = mb;
-      if (__any(mb - ref > kFrameLimit)) {
+      if (!NOFOLD && __any(mb - ref > kFrameLimit)) {
         const float r = __builtin_amdgcn_exp2f(ref - mb);
         lsum *= r;
 #pragma unroll
@@ -334,7 +337,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
           for (int e = 0; e < 16; ++e) o[cb][e] *= r;
         ref = mb;
       }
-      const float factor = __builtin_amdgcn_exp2f(mb - ref);
+      // fold factor (fixed frame), or for the ablation the usual rescale alpha = 2^(m_prev - m)
+      const float factor = NOFOLD ? (m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - mnew))
+                                  : __builtin_amdgcn_exp2f(mb - ref);
       // (each exp is followed by independent adds: the transcendental unit then overlaps them)
       float ps = 0.0f;
 #pragma unroll
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
         x[k] = __builtin_amdgcn_exp2f(x[k] - mb);
         ps += x[k];
       }
-      lsum = __builtin_fmaf(ps, factor, lsum);
+      lsum = NOFOLD ? __builtin_fmaf(factor, lsum, ps) : __builtin_fmaf(ps, factor, lsum);
       v8i pop[2];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -353,6 +358,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         v16f inner = v16f{};
+        if constexpr (NOFOLD) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) inner[r] = o[cb][r] * factor;
+        }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const uint4 v0 = *reinterpret_cast<const uint4*>(st + vofs[cb][h2][0]);
@@ -360,8 +369,12 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
           const v8i vop = {(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
           inner = mfma_fp8(vop, pop[h2], inner);
         }
+        if constexpr (NOFOLD) {
+          o[cb] = inner;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(inner[r], factor, o[cb][r]);
+          for (int r = 0; r < 16; ++r) o[cb][r] = __builtin_fmaf(inner[r], factor, o[cb][r]);
+        }
       }
       m = mnew;
     }
@@ -434,15 +447,21 @@ __global__ __launch_bounds__(256) void k_debug_qk(KArgs a) {
   }
 }
 
-template <int D, int CAUSAL>
-int launch_attn_d(const KArgs& a, hipStream_t st) {
+template <int D, int CAUSAL, int NOFOLD>
+int launch_attn_f(const KArgs& a, hipStream_t st) {
   const dim3 grid((a.Nq + kQBlock - 1) / kQBlock * a.Hq, a.B);
   switch (a.out_dtype) {
-    case SAGE2_F32: k_attn<D, CAUSAL, SAGE2_F32><<<grid, 256, 0, st>>>(a); break;
-    case SAGE2_BF16: k_attn<D, CAUSAL, SAGE2_BF16><<<grid, 256, 0, st>>>(a); break;
-    default: k_attn<D, CAUSAL, SAGE2_F16><<<grid, 256, 0, st>>>(a); break;
+    case SAGE2_F32: k_attn<D, CAUSAL, SAGE2_F32, NOFOLD><<<grid, 256, 0, st>>>(a); break;
+    case SAGE2_BF16: k_attn<D, CAUSAL, SAGE2_BF16, NOFOLD><<<grid, 256, 0, st>>>(a); break;
+    default: k_attn<D, CAUSAL, SAGE2_F16, NOFOLD><<<grid, 256, 0, st>>>(a); break;
   }
   return (int)hipGetLastError();
+}
+
+template <int D, int CAUSAL>
+int launch_attn_d(const KArgs& a, hipStream_t st) {
+  return (a.flags & SAGE2_NO_FP32_FOLD) ? launch_attn_f<D, CAUSAL, 1>(a, st)
+                                        : launch_attn_f<D, CAUSAL, 0>(a, st);
 }
 
 }  // namespace

@@ -41,7 +41,7 @@ sage2_status check_strides(const int64_t* s, int esize, bool varlen) {
 sage2_status validate(const sage2_params* p) {
   if (!p) return SAGE2_ERR_NULL;
   if (p->d < 8 || p->d > 128 || p->d % 8) return SAGE2_ERR_UNSUPPORTED;
-  if (p->flags & ~(SAGE2_NO_K_SMOOTH | SAGE2_NO_Q_SMOOTH | SAGE2_PER_BLOCK_SCALES))
+  if (p->flags & ~(SAGE2_NO_K_SMOOTH | SAGE2_NO_Q_SMOOTH | SAGE2_PER_BLOCK_SCALES | SAGE2_NO_FP32_FOLD))
     return SAGE2_ERR_UNSUPPORTED;
   if (p->in_dtype != SAGE2_F16 && p->in_dtype != SAGE2_BF16) return SAGE2_ERR_UNSUPPORTED;
   if (p->out_dtype != SAGE2_F16 && p->out_dtype != SAGE2_BF16 && p->out_dtype != SAGE2_F32)

@@ -64,7 +64,7 @@ def test_workspace_size_closed_form(lib):
     ("d", 136, sage2.ERR_UNSUPPORTED),
     ("d", 256, sage2.ERR_UNSUPPORTED),
     ("d", 0, sage2.ERR_UNSUPPORTED),
-    ("flags", 8, sage2.ERR_UNSUPPORTED),
+    ("flags", 16, sage2.ERR_UNSUPPORTED),
     ("flags", -1, sage2.ERR_UNSUPPORTED),
     ("in_dtype", sage2.F32, sage2.ERR_UNSUPPORTED),
     ("out_dtype", 7, sage2.ERR_UNSUPPORTED),
@@ -97,7 +97,7 @@ def test_head_dim_padding_layout(lib, d, padded):
 
 
 def test_ablation_flags_accepted(lib):
-    for f in (0, sage2.NO_K_SMOOTH, sage2.NO_Q_SMOOTH, sage2.PER_BLOCK_SCALES, 7):
+    for f in (0, sage2.NO_K_SMOOTH, sage2.NO_Q_SMOOTH, sage2.PER_BLOCK_SCALES, sage2.NO_FP32_FOLD, 15):
         assert _ws_status(lib, _params(flags=f))[0] == sage2.OK
 
 

@@ -132,11 +132,14 @@ def test_head_dim_padding(case):
     _full_check(W.custom(1, hq, hkv, 200, 200, d, dt, causal, seed=300 + d))
 
 
-@pytest.mark.parametrize("flags", [1, 2, 3, 4, 7], ids=["no_k_smooth", "no_q_smooth", "no_smoothing",
-                                                       "per_block_scales", "naive_per_block"])
+@pytest.mark.parametrize("flags", [1, 2, 3, 4, 7, 8], ids=["no_k_smooth", "no_q_smooth", "no_smoothing",
+                                                          "per_block_scales", "naive_per_block",
+                                                          "no_fp32_fold"])
 def test_smoothing_ablations(flags):
     """The ablation flags reproduce the oracle's ablations bit for bit (codes, scales, correction)
-    and to the usual bar on the output; accuracy against FP64 is reported by the parity check."""
+    and to the usual bar on the output; accuracy against FP64 is reported by the parity check.
+    NO_FP32_FOLD (8) is not modelled by the oracle (its result depends on the MFMA's own
+    accumulation): it is held to the two-level oracle's bar, which on gfx950 it meets."""
     w = W.custom(1, 4, 2, 300, 300, 128, torch.bfloat16, True, seed=77, k_offset_std=4.0,
                  q_offset_std=4.0)
     _full_check(w, flags=flags)
