@@ -480,7 +480,6 @@ __global__ __launch_bounds__(256) void k_delta(KArgs a) {
   __syncthreads();
   const int grp = a.Hq / a.Hkv;
   const int nqb = (s.q_len + kQBlock - 1) / kQBlock;
-  const int npairs = grp * nqb;
   const int koff = s.kv_len - s.q_len;
   const int li = lane & 15, lk = lane >> 4;
   const double L = (double)a.L;
