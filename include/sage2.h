@@ -48,7 +48,8 @@ extern "C" {
 typedef enum {
   SAGE2_OK = 0,
   SAGE2_ERR_NULL = 1,         /* a required pointer is NULL */
-  SAGE2_ERR_SHAPE = 2,        /* bad sizes: B/H/N <= 0, H_q % H_kv != 0, bad cu_seqlens, ... */
+  SAGE2_ERR_SHAPE = 2,        /* bad sizes: B/H/N <= 0, H_q % H_kv != 0, bad cu_seqlens, a workspace
+                               * whose per-head extents pass 2^31 - 1 rows or correction entries, ... */
   SAGE2_ERR_UNSUPPORTED = 3,  /* head dim not a multiple of 8 in [8, 128], unknown dtype or flag, ... */
   SAGE2_ERR_ALIGN = 4,        /* pointer or stride not 16-byte aligned; workspace not 256-byte aligned */
   SAGE2_ERR_WORKSPACE = 5,    /* ws_bytes smaller than sage2_workspace_size() */

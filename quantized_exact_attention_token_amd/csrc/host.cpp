@@ -2,6 +2,7 @@
 // Pure C++ (no HIP headers): every check here runs before any device call.
 #include <cmath>
 #include <cstdint>
+#include <climits>
 #include <cstring>
 
 #include "sage2_internal.h"
@@ -37,6 +38,8 @@ sage2_status check_strides(const int64_t* s, int esize, bool varlen) {
   return SAGE2_OK;
 }
 
+void compute_layout(const sage2_params* p, sage2_ws_layout* L);
+
 // Checks everything that does not involve a data pointer.
 sage2_status validate(const sage2_params* p) {
   if (!p) return SAGE2_ERR_NULL;
@@ -60,6 +63,13 @@ sage2_status validate(const sage2_params* p) {
       seq_lengths(p, b, &lq, &lkv);
       if (lq < 0 || lkv < 0 || lq > p->N_q || lkv > p->N_kv) return SAGE2_ERR_SHAPE;
     }
+  }
+  // the device's sequence table holds per-head workspace offsets as int32
+  {
+    sage2_ws_layout L;
+    compute_layout(p, &L);
+    const int64_t lim = INT32_MAX;
+    if (L.q_rows > lim || L.kv_rows > lim || L.q_blocks > lim || L.delta_len > lim) return SAGE2_ERR_SHAPE;
   }
   const int ei = elem_size(p->in_dtype), eo = elem_size(p->out_dtype);
   sage2_status st;

@@ -174,3 +174,17 @@ def test_status_strings(lib):
     for s in range(7):
         assert len(sage2.status_string(s)) > 0
     assert sage2.status_string(99) == "unknown status"
+
+
+def test_rejects_layouts_past_int32(lib):
+    """Per-head workspace extents are carried as int32 on the device: a dense shape whose correction
+    table would pass 2^31 - 1 entries per head is refused before any sizing overflow."""
+    p = _params(N_q=200_000, N_kv=200_000, B=8)   # 8 * 1563 Q blocks * 200064 keys > 2^31
+    for name in ("q_stride", "o_stride"):
+        getattr(p, name)[:] = (200_000 * 8 * 128, 8 * 128, 128)
+    for name in ("k_stride", "v_stride"):
+        getattr(p, name)[:] = (200_000 * 2 * 128, 2 * 128, 128)
+    assert _ws_status(lib, p)[0] == sage2.ERR_SHAPE
+    p.B = 1   # 1563 * 200064 = 3.1e8 entries per head: fine
+    assert _ws_status(lib, p)[0] == sage2.OK
+
