@@ -38,6 +38,11 @@ constexpr float kLog2_448 = 8.80735492205760410750f;
 // largest fold factor exponent before the running output is renormalized: o and l then stay below
 // 2^(64 + 27) for any sequence the ABI accepts
 constexpr float kFrameLimit = 64.0f;
+// start (and floor) of the running row max: a row with no visible key yet keeps this finite max
+// (its p are exact zeros), and the output frame starts at its frame, so the first tile with a visible
+// key always takes the renormalization (o and l are still zero then); for the single-level ablation
+// its alpha 2^(m_prev - m) is 0 there. Logits below -2^100 are outside the supported range.
+constexpr float kMaxFloor = -0x1p100f;
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -46,12 +51,22 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// v_max3_f32 written out. Through fmaxf the compiler quiets every operand that it cannot prove to be
+// the result of arithmetic (here the two permlane results): one extra instruction each on the
+// softmax's critical path. (Not used for the long in-lane chain: after each inline asm the compiler
+// adds a wait state.)
+__device__ inline float max3(float a, float b, float c) {
+  float y;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(y) : "v"(a), "v"(b), "v"(c));
+  return y;
+}
+
 // max over lanes l and l ^ 32 (the two half-waves hold the two key halves of a query's row):
 // v_permlane32_swap exchanges the half-waves, and whichever of its two results holds the other
 // half's value, the max over both and the lane's own value is the pair max
 __device__ inline float half_wave_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  return max3(x, __uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <int OUT>
@@ -126,8 +141,8 @@ __device__ inline int v_block(int h2, int c, int j) {
 // Per-lane byte offsets (relative to a tile's global base) of the blocks this lane fetches.
 template <int D>
 struct DmaPlan {
-  int k[(Stage<D>::K_INSTR + 3) / 4];
-  int v[(Stage<D>::V_INSTR + 3) / 4];
+  uint32_t k[(Stage<D>::K_INSTR + 3) / 4];
+  uint32_t v[(Stage<D>::V_INSTR + 3) / 4];
 };
 
 template <int D>
@@ -150,8 +165,15 @@ __device__ inline DmaPlan<D> make_dma_plan(int wave, int lane) {
   return pl;
 }
 
-__device__ inline void dma16(const void* src, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// 16-byte global->LDS DMA through a buffer descriptor over one tile: the tile's base sits in scalar
+// registers and the lane's byte offset in one loop-invariant VGPR, so issuing it needs no vector
+// address arithmetic. 0x00020000 is the gfx9-family descriptor word 3 (32-bit data format, no
+// swizzle); offsets are checked against `bytes` (out of range reads return zero).
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, off, 0, 0, 0);
 }
 
 // Issues the DMA of tile t into stage `st` (every wave its share).
@@ -160,19 +182,20 @@ __device__ inline void issue_tile(const DmaPlan<D>& pl, int wave, int lane, int 
                                   const uint8_t* kcode, const uint8_t* v8, const float* drow,
                                   const float* skp) {
   using S = Stage<D>;
-  const uint8_t* kt = kcode + (int64_t)t * kBN * S::CB;
-  const uint8_t* vt = v8 + (int64_t)t * kBN * D;
+  const auto kr = tile_rsrc(kcode + (int64_t)t * kBN * S::CB, kBN * S::CB);
+  const auto vr = tile_rsrc(v8 + (int64_t)t * kBN * D, kBN * D);
 #pragma unroll
   for (int u = 0; u < (S::K_INSTR + 3) / 4; ++u)
-    if (wave + 4 * u < S::K_INSTR) dma16(kt + pl.k[u], st + S::K_OFF + (wave + 4 * u) * 1024);
+    if (wave + 4 * u < S::K_INSTR) dma16(kr, pl.k[u], st + S::K_OFF + (wave + 4 * u) * 1024);
 #pragma unroll
   for (int u = 0; u < (S::V_INSTR + 3) / 4; ++u)
-    if (wave + 4 * u < S::V_INSTR) dma16(vt + pl.v[u], st + S::V_OFF + (wave + 4 * u) * 1024);
+    if (wave + 4 * u < S::V_INSTR) dma16(vr, pl.v[u], st + S::V_OFF + (wave + 4 * u) * 1024);
   if (wave == 0) {
     // one select of two in-bounds addresses (no divergent branch around the DMA)
     const float* dsrc = drow + t * kBN + 4 * (lane & 31);
     const float* ssrc = skp + 8 * t + 4 * (lane & 1);
-    dma16((unsigned)(lane - 32) < 2u ? ssrc : dsrc, st + S::D_OFF);
+    __builtin_amdgcn_global_load_lds((unsigned)(lane - 32) < 2u ? ssrc : dsrc,
+                                     (__attribute__((address_space(3))) void*)(st + S::D_OFF), 16, 0, 0);
   }
 }
 
@@ -250,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const float* drow = ws_ptr<float>(a, a.lay.delta) + (int64_t)h * a.lay.delta_len + s.delta0 +
                       (int64_t)qb * kvpad;
 
-  float m = kNegInf, lsum = 0.0f, ref = 0.0f;
+  float m = kMaxFloor, lsum = 0.0f, ref = kMaxFloor - kLog2_448;
   v16f o[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = v16f{};
@@ -287,8 +310,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
       for (int sub = 0; sub < 4; ++sub) {
         v16f acc = v16f{};
         if constexpr (D == 128) {
-          // this lane's 48 bytes of the key row (rows keep their 3-block halves contiguous), read
-          // as 16+8 and 8+16 bytes so each 24-byte operand lands in one register tuple
+          // this lane's 48 bytes of the key row (rows keep their 3-block halves contiguous). The
+          // compiler merges the two middle 8-byte reads into one 16-byte read and splits it over
+          // the two operand tuples with two register copies; keeping the reads apart removes the
+          // copies but costs a fourth LDS read per subtile, which measured slower
           const uint4 b0 = *reinterpret_cast<const uint4*>(st + kofs[sub]);
           const uint2 b1 = *reinterpret_cast<const uint2*>(st + kofs[sub] + 16);
           const uint2 b2 = *reinterpret_cast<const uint2*>(st + kofs[sub] + 24);
@@ -319,15 +344,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
           x[k] = vis ? x[k] : kNegInf;
         }
       }
-      float mt = x[0];
+      // running max over the previous value and this tile's keys, then over the two half-waves
+      float mt = m;
 #pragma unroll
-      for (int k = 1; k < 64; ++k) mt = fmaxf(mt, x[k]);
-      mt = half_wave_max(mt);
-      const float mnew = fmaxf(m, mt);
-      const float mb = (mnew == kNegInf) ? 0.0f : mnew - kLog2_448;
-      // the output frame starts at the first tile with a visible key; renormalize (rarely) before
-      // the fold factor 2^(mb - ref) could leave the f32 range
-      if (m == kNegInf) ref = mb;
+      for (int k = 0; k < 64; ++k) mt = fmaxf(mt, x[k]);
+      const float mnew = half_wave_max(mt);
+      const float mb = mnew - kLog2_448;
+      // renormalize (rarely: at the first visible key, then on large rises of the max) before the
+      // fold factor 2^(mb - ref) could leave the f32 range
       if (!NOFOLD && __any(mb - ref > kFrameLimit)) {
         const float r = __builtin_amdgcn_exp2f(ref - mb);
         lsum *= r;
@@ -338,8 +362,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
         ref = mb;
       }
       // fold factor (fixed frame), or for the ablation the usual rescale alpha = 2^(m_prev - m)
-      const float factor = NOFOLD ? (m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - mnew))
-                                  : __builtin_amdgcn_exp2f(mb - ref);
+      const float factor = NOFOLD ? __builtin_amdgcn_exp2f(m - mnew) : __builtin_amdgcn_exp2f(mb - ref);
       // (each exp is followed by independent adds: the transcendental unit then overlaps them)
       float ps = 0.0f;
 #pragma unroll
