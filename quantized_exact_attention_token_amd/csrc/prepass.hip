@@ -450,7 +450,8 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <int D, int IN>
-__global__ __launch_bounds__(256) void k_delta(KArgs a) {
+// (at most 128 VGPRs: four workgroups per CU, as many as the LDS tile allows, instead of three)
+__global__ __launch_bounds__(256, 4) void k_delta(KArgs a) {
   constexpr int KS = D + 4;  // floats per k~ row in LDS
   // blockIdx.x = tile * H_kv + kv head: under a causal mask the early key tiles carry the most
   // (q head, Q block) pairs, and this order dispatches them first (longest first)
