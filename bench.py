@@ -5,6 +5,7 @@ correction table) then sage2_attn_fwd (INT4 QK^T, online softmax, FP8 P~V with t
 with the inputs already resident in HBM. Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa16k] [--no-cpu-baseline]
+                    [--no-clock]
 
 value = attention ops (4*Nq*Nkv*d per sequence and q head, halved under a causal mask) per second
 of the whole step; `kernel_tops` is the same count over sage2_attn_fwd alone (the kernel-only
@@ -25,6 +26,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "attention TOPS at d=128 N=4K-32K (1 GPU), % of i8/fp8 MFMA peak; err vs oracle"
 PEAK_TOPS = 5000.0          # MI355X dense int8 (and fp8) MFMA peak, TOPS
+NOMINAL_MHZ = 2400.0        # the engine clock that peak is quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_gqa16k_traffic.json")
 
 
@@ -47,6 +49,47 @@ def traffic_per_launch(workload: str):
     if t.get("kernel_source_digest") != kernel_source_digest() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
+
+
+def gfx_clock_under_load(launch, settle_s: float = 1.0, limit_s: float = 20.0):
+    """Mean GFX clock (MHz over the XCDs) that amd-smi reports while `launch` runs back to back, or
+    None where amd-smi is missing or fails. amd-smi runs as a child process; the launches go on
+    until it has answered (at most `limit_s`)."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(smi):
+        return None
+    got = {}
+
+    def sample():
+        time.sleep(settle_s)
+        try:
+            p = subprocess.run([smi, "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                               text=True, timeout=15)
+            got["out"] = p.stdout
+        except (OSError, subprocess.SubprocessError):
+            pass
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < limit_s:
+        for _ in range(50):
+            launch()
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    try:
+        data = json.loads(got["out"])
+        clocks = data["gpu_data"][0]["clock"]
+        mhz = [v["clk"]["value"] for k, v in clocks.items() if k.startswith("gfx_")]
+        return sum(mhz) / len(mhz) if mhz else None
+    except (KeyError, IndexError, TypeError, ValueError):
+        return None
 
 
 def cpu_baseline(run, w, budget_s: float = 20.0):
@@ -97,6 +140,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi clock sample (a few seconds of extra attention launches)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: time sage2_attn_fwd on the d=128 length "
                          "sweep (N = 4K..32K, causal and not) and print one JSON line with a row "
@@ -189,6 +234,9 @@ def main():
     kernel_tops = ops / (att_avg * 1e-3) / 1e12
     value = ops / (ms_step * 1e-3) / 1e12
 
+    # the clock the kernel actually ran at (amd-smi, sampled under a back-to-back attention load
+    # after the timed steps); the peak scales with it
+    clock = None if args.no_clock else gfx_clock_under_load(run.attn)
     traffic = traffic_per_launch(w.name)
     roofline = {"bound": "mfma", "achieved": kernel_tops, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": kernel_tops / PEAK_TOPS, "traffic": traffic,
@@ -207,6 +255,9 @@ def main():
         "kernel_tops": kernel_tops,
         "kernel_frac_of_peak": kernel_tops / PEAK_TOPS,
         "attn_ms": {"avg": att_avg, "min": att_ms[0], "median": att_ms[len(att_ms) // 2]},
+        "gfx_clock_mhz": clock,
+        "kernel_frac_of_peak_at_clock": (kernel_tops / (PEAK_TOPS * clock / NOMINAL_MHZ)
+                                         if clock else None),
         "prepass_ms": {"avg": sum(pre_ms) / len(pre_ms), "min": pre_ms[0]},
         "roofline": roofline,
     }
