@@ -136,8 +136,11 @@ def cpu_baseline(run, w, budget_s: float = 20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the first ~100 ms of GPU work after idle run slower (at gqa16k, 5 warm-up steps left the
+    # attention average at 1.23 ms, 200 at 1.18 ms): the default warm-up (200 steps, about 0.3 s
+    # at gqa16k) keeps them out of the timed steps
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gqa16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
@@ -177,8 +180,14 @@ def main():
         for name, w in W.SWEEP.items():
             run = H.GpuRun(w)
             run.prepass()
-            for _ in range(max(1, args.warmup)):
-                run.attn()
+            # warm-up: at least --warmup calls and at least 0.3 s of back-to-back calls
+            t_w = time.perf_counter()
+            n_w = 0
+            while n_w < max(1, args.warmup) or time.perf_counter() - t_w < 0.3:
+                for _ in range(10):
+                    run.attn()
+                n_w += 10
+                torch.cuda.synchronize()
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.steps)]
             stream = torch.cuda.current_stream()
