@@ -342,8 +342,10 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
 __device__ inline int tile_key(int h, int s) { return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * h + (s & 3); }
 
 // ---- K: per-16-key-group INT4 codes; V: FP8 codes in the attention kernel's tile layout -------
-// grid (64-key tiles, H_kv, B), block 256. The tile's K and V rows are staged in LDS with 16-byte
-// loads (zero past the sequence end). Wave w quantizes K group w of the tile: the 16 keys of
+// grid (64-key tiles, H_kv, B), block 256. The tile's K rows are staged in LDS with 16-byte loads
+// (zero past the sequence end); V is scaled and converted to FP8 in registers (each thread one
+// 16-byte chunk of the keys of 4 or 2 consecutive output slots) and transposed through LDS as
+// bytes, then copied out in 32-byte rows. Wave w quantizes K group w of the tile: the 16 keys of
 // 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half owns), D/32 lanes
 // per key with 32 channels each; the smoothed values stay in registers between the group max and
 // the codes.
@@ -357,7 +359,9 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
   __shared__ __attribute__((aligned(16))) float kbar[D];
   __shared__ float svinv[D];
   __shared__ __attribute__((aligned(16))) uint16_t kr[kKVTile][D];
-  __shared__ float vt[kKVTile][D + 1];
+  // V codes in the output order: for channel c and lane half h, the 32 fp8 bytes of the keys
+  // tile_key(h, 0..31), at byte 32 (2c + h)
+  __shared__ __attribute__((aligned(16))) uint32_t vt8[2 * D * 32 / 4];
   const int64_t sidx = ((int64_t)b * a.Hkv + g) * D;
   if (tid < D) {
     kbar[tid] = ws_ptr<float>(a, a.lay.kbar)[sidx + tid];
@@ -365,19 +369,37 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
   }
   const int n = max(0, min(kKVTile, s.kv_len - t * kKVTile));
   stage_rows<D, kKVTile>(kr, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n, a.dt);
+  // V: this thread's 16-byte chunk (channels 8 ch + [0, 8)) of KPT keys that are consecutive both
+  // in the tile and in the output order (slots s0 .. s0 + KPT - 1 of lane half h)
+  constexpr int RW = D / 8;
+  constexpr int KPT = kKVTile * RW / 256;
+  constexpr int NG = 32 / KPT;
+  const int ch = tid % RW, grp = tid / RW, h = grp / NG, s0 = KPT * (grp % NG);
+  const int key0 = tile_key(h, s0);
+  uint4 vr[KPT];
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    vr[e] = make_uint4(0, 0, 0, 0);
+    if (key0 + e < n && 8 * ch < a.dt)
+      vr[e] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.v) +
+                                              row_index(a.vs, b, s.kv_start + t * kKVTile + key0 + e, g) +
+                                              8 * ch);
+  }
   __syncthreads();
-  // V rows, scaled per channel (f32), into vt
   {
-    constexpr int RW = D / 8;
-    uint4 v[kKVTile * RW / 256];
-    load_rows<D, kKVTile>(v, a.v, a.vs, b, s.kv_start + t * kKVTile, g, n, a.dt);
+    float f[KPT][8];
 #pragma unroll
-    for (int k = 0; k < kKVTile * RW / 256; ++k) {
-      const int idx = tid + 256 * k, key = idx / RW, ch = idx % RW;
-      float f[8];
-      widen8<IN>(v[k], f);
+    for (int e = 0; e < KPT; ++e) widen8<IN>(vr[e], f[e]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[key][8 * ch + e] = f[e] * svinv[8 * ch + e];
+    for (int i = 0; i < 8; ++i) {
+      const int c = 8 * ch + i;
+      const float sc = svinv[c];
+      const int w = cvt_fp8x2(f[0][i] * sc, f[1][i] * sc, 0, false);
+      if constexpr (KPT == 4) {
+        vt8[((2 * c + h) * 32 + s0) / 4] = (uint32_t)cvt_fp8x2(f[2][i] * sc, f[3][i] * sc, w, true);
+      } else {
+        reinterpret_cast<uint16_t*>(vt8)[((2 * c + h) * 32 + s0) / 2] = (uint16_t)w;
+      }
     }
   }
   // K group of this wave: its 16 keys, LPR lanes per key with 32 channels each (for D = 64 the
@@ -419,17 +441,10 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
   uint8_t* v8 = ws_ptr<uint8_t>(a, a.lay.v8) +
                 ((int64_t)g * (a.lay.kv_rows / kKVTile) + s.kv_row0 / kKVTile + t) * (kKVTile * D);
   for (int p = tid; p < 2 * D; p += 256) {
-    const int c = p >> 1, h = p & 1;
-    int w[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int s0 = 4 * q;
-      int x = cvt_fp8x2(vt[tile_key(h, s0)][c], vt[tile_key(h, s0 + 1)][c], 0, false);
-      w[q] = cvt_fp8x2(vt[tile_key(h, s0 + 2)][c], vt[tile_key(h, s0 + 3)][c], x, true);
-    }
+    const uint4* src = reinterpret_cast<const uint4*>(vt8) + 2 * p;
     uint4* dst = reinterpret_cast<uint4*>(v8 + (int64_t)p * 32);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    dst[0] = src[0];
+    dst[1] = src[1];
   }
 }
 
