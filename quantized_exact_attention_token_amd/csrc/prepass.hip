@@ -342,26 +342,29 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
 __device__ inline int tile_key(int h, int s) { return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * h + (s & 3); }
 
 // ---- K: per-16-key-group INT4 codes; V: FP8 codes in the attention kernel's tile layout -------
-// grid (64-key tiles, H_kv, B), block 256. The tile's K rows are staged in LDS with 16-byte loads
-// (zero past the sequence end); V is scaled and converted to FP8 in registers (each thread one
-// 16-byte chunk of the keys of 4 or 2 consecutive output slots) and transposed through LDS as
-// bytes, then copied out in 32-byte rows. Wave w quantizes K group w of the tile: the 16 keys of
-// 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half owns), D/32 lanes
-// per key with 32 channels each; the smoothed values stay in registers between the group max and
-// the codes.
+// One workgroup of 256 per (64-key tile, kv head, sequence). The tile's K rows are staged in LDS
+// with 16-byte loads (zero past the sequence end); V is scaled and converted to FP8 in registers
+// (each thread one 16-byte chunk of the keys of 4 or 2 consecutive output slots) and transposed
+// through LDS as bytes, then copied out in 32-byte rows. Wave w quantizes K group w of the tile:
+// the 16 keys of 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half
+// owns), D/32 lanes per key with 32 channels each; the smoothed values stay in registers between
+// the group max and the codes.
+// LDS bytes of one K/V quantizer workgroup: kbar, 1/s_v (D floats each), the K rows (kKVTile x D
+// raw elements), and the V codes in the output order (for channel c and lane half h the 32 fp8
+// bytes of the keys tile_key(h, 0..31), at byte 32 (2c + h))
+template <int D>
+constexpr int kQuantKvLds = 8 * D + 2 * kKVTile * D + 64 * D;
+
 template <int D, int IN>
-__global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
-  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_t* lds) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seq s = load_seq(a, b);
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
   if (t * kKVTile >= kvpad) return;
-  __shared__ __attribute__((aligned(16))) float kbar[D];
-  __shared__ float svinv[D];
-  __shared__ __attribute__((aligned(16))) uint16_t kr[kKVTile][D];
-  // V codes in the output order: for channel c and lane half h, the 32 fp8 bytes of the keys
-  // tile_key(h, 0..31), at byte 32 (2c + h)
-  __shared__ __attribute__((aligned(16))) uint32_t vt8[2 * D * 32 / 4];
+  float* kbar = reinterpret_cast<float*>(lds);
+  float* svinv = kbar + D;
+  uint16_t(*kr)[D] = reinterpret_cast<uint16_t(*)[D]>(lds + 8 * D);
+  uint32_t* vt8 = reinterpret_cast<uint32_t*>(lds + 8 * D + 2 * kKVTile * D);
   const int64_t sidx = ((int64_t)b * a.Hkv + g) * D;
   if (tid < D) {
     kbar[tid] = ws_ptr<float>(a, a.lay.kbar)[sidx + tid];
@@ -456,27 +459,27 @@ __global__ __launch_bounds__(256) void k_quant_kv(KArgs a) {
 // cancellation-heavy inputs), so feeding it the channels four at a time, in order, is exactly
 // the channel-order chain. Operand layouts: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k,
 // D[i][j] in lane j + 16 (i % 4), register i / 4.
-// grid (64-key tiles x H_kv, 1, B), block 256: k~ of the tile in LDS (f32, a 4-float row skew). Only
-// the (q head, Q block) pairs that see a key of the tile are computed: they are numbered Q block
-// major and dealt to the waves in blocks of 32 pairs x the 64 keys = 2 x 4 MFMA tiles, so a causal
-// mask leaves no wave idle. Entries a causal mask hides from every row of a Q block are left
-// unwritten (the attention kernel masks such keys by selection, never reads them into arithmetic
-// that reaches the output) except within a computed tile, where they are stored as 0.
+// One workgroup of 256 per (64-key tile, kv head, sequence): k~ of the tile in LDS (f32, a 4-float
+// row skew). Only the (q head, Q block) pairs that see a key of the tile are computed: they are
+// numbered Q block major and dealt to the waves in blocks of 32 pairs x the 64 keys = 2 x 4 MFMA
+// tiles, so a causal mask leaves no wave idle. Entries a causal mask hides from every row of a Q
+// block are left unwritten (the attention kernel masks such keys by selection, never reads them
+// into arithmetic that reaches the output) except within a computed tile, where they are stored as
+// 0.
 typedef double v4d __attribute__((ext_vector_type(4)));
 
+// LDS bytes of one correction-table workgroup: the tile's k~ rows of D + 4 floats
+template <int D>
+constexpr int kDeltaLds = 4 * kKVTile * (D + 4);
+
 template <int D, int IN>
-// (at most 128 VGPRs: four workgroups per CU, as many as the LDS tile allows, instead of three)
-__global__ __launch_bounds__(256, 4) void k_delta(KArgs a) {
+__device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt) {
   constexpr int KS = D + 4;  // floats per k~ row in LDS
-  // blockIdx.x = tile * H_kv + kv head: under a causal mask the early key tiles carry the most
-  // (q head, Q block) pairs, and this order dispatches them first (longest first)
-  const int t = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Seq s = load_seq(a, b);
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
   if (t * kKVTile >= kvpad) return;
-  __shared__ __attribute__((aligned(16))) float kt[kKVTile * KS];
   const float* kbar = ws_ptr<float>(a, a.lay.kbar) + ((int64_t)b * a.Hkv + g) * D;
   {
     // k~ = k - kbar in f32 (keys past the sequence end: 0)
@@ -585,6 +588,23 @@ __global__ __launch_bounds__(256, 4) void k_delta(KArgs a) {
   }
 }
 
+// ---- the K/V quantizer and the correction table in one launch ----------------------------------
+// The two read the statistics of the previous kernels and not each other's output; run side by
+// side, the HBM-bound quantizer workgroups fill the CUs next to the fp64-MFMA-bound correction
+// workgroups as the correction workgroups drain. grid (2 x 64-key tiles x H_kv, 1, B): first the
+// correction workgroups, x = tile * H_kv + kv head (longest first under a causal mask), then the
+// quantizer workgroups in the same order. (Quantizers first, or the two roles interleaved, measured
+// slower: the interleaved order stretched the pre-pass by half.) At most 128 VGPRs: four
+// workgroups per CU, as many as the correction tile's LDS allows.
+template <int D, int IN>
+__global__ __launch_bounds__(256, 4) void k_kv_delta(KArgs a, int n_tiles) {
+  constexpr int LDS = kDeltaLds<D> > kQuantKvLds<D> ? kDeltaLds<D> : kQuantKvLds<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+  const int n = n_tiles * a.Hkv, x = blockIdx.x;
+  if (x < n) delta_tile<D, IN>(a, x / a.Hkv, x % a.Hkv, blockIdx.z, reinterpret_cast<float*>(lds));
+  else quant_kv_tile<D, IN>(a, (x - n) / a.Hkv, (x - n) % a.Hkv, blockIdx.z, lds);
+}
+
 template <int D, int IN>
 int launch_all(const KArgs& a, hipStream_t st) {
   const int nch = (a.Nkv + kKVPad - 1) / kKVPad;
@@ -594,8 +614,7 @@ int launch_all(const KArgs& a, hipStream_t st) {
   k_kstats<D, IN><<<dim3(nch, a.Hkv, a.B), 256, 0, st>>>(a);
   k_kreduce<D><<<dim3(D / 32, a.Hkv, a.B), 256, 0, st>>>(a);
   k_quant_q<D, IN><<<dim3(nqb, a.Hq, a.B), 256, 0, st>>>(a);
-  k_quant_kv<D, IN><<<dim3(ntile, a.Hkv, a.B), 256, 0, st>>>(a);
-  k_delta<D, IN><<<dim3(ntile * a.Hkv, 1, a.B), 256, 0, st>>>(a);
+  k_kv_delta<D, IN><<<dim3(2 * ntile * a.Hkv, 1, a.B), 256, 0, st>>>(a, ntile);
   return (int)hipGetLastError();
 }
 
