@@ -119,20 +119,24 @@ __device__ inline void stage_rows(uint16_t (*dst)[D], const void* base, const in
 }
 
 // ---- K channel sums and V channel max over one 128-token chunk ---------------------------------
-// grid (chunks, H_kv, B), block 256. The chunk's K rows are staged in LDS (zero rows past the
-// sequence end add +0.0, which leaves an fp64 sum unchanged); threads c < D then sum channel c in
-// token order. V's channel max needs no order: each thread keeps the max of the 8 channels it
-// loads, and threads D..2D-1 combine them.
+// One workgroup of 256 per (128-key chunk, kv head, sequence). The chunk's K rows are staged in LDS
+// (zero rows past the sequence end add +0.0, which leaves an fp64 sum unchanged); threads c < D
+// then sum channel c in token order. V's channel max needs no order: each thread keeps the max of
+// the 8 channels it loads, and threads D..2D-1 combine them.
+// LDS bytes: the chunk's K rows (kKVPad x D raw elements), then 256 / (D / 8) rows of D floats
+template <int D>
+constexpr int kKstatsLds = 2 * kKVPad * D + 4 * (256 / (D / 8)) * D;
+
 template <int D, int IN>
-__global__ __launch_bounds__(256) void k_kstats(KArgs a) {
+__device__ inline void kstats_chunk(const KArgs& a, int u, int g, int b, uint8_t* lds) {
   constexpr int RW = D / 8;
   constexpr int RPP = 256 / RW;  // rows per pass of the block over the chunk
-  const int u = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const Seq s = load_seq(a, b);
   if (u * kKVPad >= s.kv_len) return;
   const int j0 = u * kKVPad, n = min(kKVPad, s.kv_len - j0);
-  __shared__ __attribute__((aligned(16))) uint16_t kr[kKVPad][D];
-  __shared__ float vm[RPP][D];
+  uint16_t(*kr)[D] = reinterpret_cast<uint16_t(*)[D]>(lds);
+  float(*vm)[D] = reinterpret_cast<float(*)[D]>(lds + 2 * kKVPad * D);
   stage_rows<D, kKVPad>(kr, a.k, a.ks, b, s.kv_start + j0, g, n, a.dt);
   {
     // V: this thread's chunks all share channels 8 (tid % RW) + [0, 8) (256 is a multiple of RW)
@@ -263,20 +267,23 @@ __device__ inline void widen32(const uint16_t* p, float (&f)[32]) {
 }
 
 // ---- Q: block mean, per-token INT4 codes -------------------------------------------------------
-// grid (Q blocks, H_q, B), block 256. The block's rows are read once, coalesced, into LDS (rows past
-// the sequence end are zero and add +0.0 to the fp64 sums); thread c sums channel c in row order.
-// The rows are then quantized with D/32 lanes per row and 32 channels per lane (one scale per
-// token: on gfx950 a lane owns one query column of the S^T = K Q^T MFMA tile, so the per-thread
-// group is one token).
+// One workgroup of 256 per (Q block, q head, sequence). The block's rows are read once, coalesced,
+// into LDS (rows past the sequence end are zero and add +0.0 to the fp64 sums); thread c sums
+// channel c in row order. The rows are then quantized with D/32 lanes per row and 32 channels per
+// lane (one scale per token: on gfx950 a lane owns one query column of the S^T = K Q^T MFMA tile,
+// so the per-thread group is one token).
+// LDS bytes: the block's Q rows (kQBlock x D raw elements), then the D block means (f32)
+template <int D>
+constexpr int kQuantQLds = 2 * kQBlock * D + 4 * D;
+
 template <int D, int IN>
-__global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__device__ inline void quant_q_block(const KArgs& a, int qb, int h, int b, uint8_t* lds) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const Seq s = load_seq(a, b);
   if (qb * kQBlock >= s.q_len) return;
   const int i0 = qb * kQBlock, n = min(kQBlock, s.q_len - i0);
-  __shared__ __attribute__((aligned(16))) uint16_t rows[kQBlock][D];
-  __shared__ __attribute__((aligned(16))) float qbar[D];
+  uint16_t(*rows)[D] = reinterpret_cast<uint16_t(*)[D]>(lds);
+  float* qbar = reinterpret_cast<float*>(lds + 2 * kQBlock * D);
   stage_rows<D, kQBlock>(rows, a.q, a.qs, b, s.q_start + i0, h, n, a.dt);
   __syncthreads();
   if (tid < D) {
@@ -340,6 +347,19 @@ __global__ __launch_bounds__(256) void k_quant_q(KArgs a) {
 // Key index (within a 64-key tile) held in slot s of lane half h: the S^T accumulator of the
 // 32x32 MFMA gives lane half h the rows 8*(r/4) + 4*h + r%4 of each 32-key subtile.
 __device__ inline int tile_key(int h, int s) { return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * h + (s & 3); }
+
+// ---- the K/V statistics and the Q quantizer in one launch ---------------------------------------
+// Both read only the inputs (and the sequence table): grid (128-key chunks x H_kv + Q blocks x
+// H_q, 1, B), first the statistics workgroups (x = chunk * H_kv + kv head), then the Q blocks
+// (x = block * H_q + q head).
+template <int D, int IN>
+__global__ __launch_bounds__(256) void k_stats_quant_q(KArgs a, int n_chunks) {
+  constexpr int LDS = kKstatsLds<D> > kQuantQLds<D> ? kKstatsLds<D> : kQuantQLds<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+  const int n = n_chunks * a.Hkv, x = blockIdx.x;
+  if (x < n) kstats_chunk<D, IN>(a, x / a.Hkv, x % a.Hkv, blockIdx.z, lds);
+  else quant_q_block<D, IN>(a, (x - n) / a.Hq, (x - n) % a.Hq, blockIdx.z, lds);
+}
 
 // ---- K: per-16-key-group INT4 codes; V: FP8 codes in the attention kernel's tile layout -------
 // One workgroup of 256 per (64-key tile, kv head, sequence). The tile's K rows are staged in LDS
@@ -611,9 +631,8 @@ int launch_all(const KArgs& a, hipStream_t st) {
   const int nqb = (a.Nq + kQBlock - 1) / kQBlock;
   const int ntile = nch * (kKVPad / kKVTile);
   k_plan<<<1, 64, 0, st>>>(a);
-  k_kstats<D, IN><<<dim3(nch, a.Hkv, a.B), 256, 0, st>>>(a);
+  k_stats_quant_q<D, IN><<<dim3(nch * a.Hkv + nqb * a.Hq, 1, a.B), 256, 0, st>>>(a, nch);
   k_kreduce<D><<<dim3(D / 32, a.Hkv, a.B), 256, 0, st>>>(a);
-  k_quant_q<D, IN><<<dim3(nqb, a.Hq, a.B), 256, 0, st>>>(a);
   k_kv_delta<D, IN><<<dim3(2 * ntile * a.Hkv, 1, a.B), 256, 0, st>>>(a, ntile);
   return (int)hipGetLastError();
 }
