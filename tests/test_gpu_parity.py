@@ -144,3 +144,34 @@ def test_smoothing_ablations(flags):
                  q_offset_std=4.0)
     _full_check(w, flags=flags)
 
+
+
+def _random_case(seed):
+    """A seeded mixed configuration: batch or packed variable-length sequences (empty ones
+    included), GQA groups of 1, 2 or 4, any head dim that is a multiple of 8, either input dtype,
+    causal or not, different Q and KV lengths when dense."""
+    rng = np.random.default_rng(1000 + seed)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    d = 8 * int(rng.integers(1, 17))
+    dt = torch.float16 if rng.integers(2) else torch.bfloat16
+    causal = bool(rng.integers(2))
+    if rng.integers(2):
+        lens = [int(x) for x in rng.integers(1, 420, size=int(rng.integers(2, 5)))]
+        if len(lens) > 2 and rng.integers(2):
+            lens[int(rng.integers(len(lens)))] = 0
+        n = max(lens)
+        return W.custom(len(lens), hq, hkv, n, n, d, dt, causal, seed=seed, seqlens=lens)
+    b = int(rng.integers(1, 3))
+    nq, nkv = int(rng.integers(1, 420)), int(rng.integers(1, 420))
+    return W.custom(b, hq, hkv, nq, nkv, d, dt, causal, seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_configurations(seed):
+    """Eight seeded mixed configurations through the whole path (the pre-pass's two fused launches
+    split their grids by role, so shapes that leave some roles empty are included)."""
+    w = _random_case(seed)
+    print(f"[parity] random {seed}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Nq{w.Nq} Nkv{w.Nkv} d{w.d} "
+          f"{str(w.dtype).split('.')[-1]} causal={w.causal} seqlens={w.seqlens}", flush=True)
+    _full_check(w)
