@@ -127,10 +127,33 @@ def cpu_baseline(run, w, budget_s: float = 20.0):
     err = {"max_abs": float(e.max()), "max_abs_beyond_tolerance": float(max(0.0, (e - tol).max())),
            "within_tolerance": bool((e <= tol).all()), "cos": H.cos(gpu, ref),
            "rows": int(nrows), "heads": int(q.shape[0])}
+    # the oracle's plain FP64 attention on a slice of the same rows (about 2 s of work)
+    t0 = time.perf_counter()
+    O.attn_fp64(q, k, v, w.causal, rows=probe, nthreads=threads)
+    t_probe64 = (time.perf_counter() - t0) / len(probe)
+    n64 = int(max(8, min(nrows, 2.0 / max(t_probe64, 1e-6))))
+    rows64 = np.linspace(0, lq - 1, n64).astype(np.int32)
+    t0 = time.perf_counter()
+    O.attn_fp64(q, k, v, w.causal, rows=rows64, nthreads=threads)
+    t_64 = time.perf_counter() - t0
+    vis64 = np.minimum(rows64 + (lk - lq), lk - 1) + 1 if w.causal else np.full(len(rows64), lk)
+    ops64 = 4.0 * q.shape[0] * float(np.sum(np.maximum(vis64, 0))) * w.d
+    # the whole quantized pipeline on the smallest workload, one thread
+    import quantized_exact_attention_token_amd.workloads as WL
+    tw = WL.WORKLOADS["tiny"]
+    tq, tk, tv, _ = WL.generate(tw)
+    tq, tk, tv = (x[0].transpose(0, 1).float().contiguous().numpy() for x in (tq, tk, tv))
+    t0 = time.perf_counter()
+    O.attn_quant(O.quantize(tq, tk, tv, nthreads=1), tw.causal, nthreads=1)
+    t_tiny = time.perf_counter() - t0
     return ({"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
              "sample": f"kv head 0 with its {q.shape[0]} q heads: full pre-pass, then attention "
                        f"for {nrows} evenly spaced query rows; ops counted for those rows only, "
-                       f"time = pre-pass + rows ({t_q:.1f}s + {t_a:.1f}s)"}, err)
+                       f"time = pre-pass + rows ({t_q:.1f}s + {t_a:.1f}s)",
+             "fp64_exact_value": ops64 / t_64 / 1e12,
+             "fp64_exact_sample": f"the oracle's plain FP64 softmax(QK^T)V on {n64} of those rows "
+                                  f"({t_64:.1f}s)",
+             "single_thread_tiny_ms": t_tiny * 1e3}, err)
 
 
 def main():
