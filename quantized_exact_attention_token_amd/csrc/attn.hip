@@ -337,11 +337,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
         }
       }
       if (need_mask) {
+        // register k holds key t*kBN + 4*hh + off(k), off(k) a constant: one compare of the
+        // constant with the lane's last visible offset per element
+        int lim = s.kv_len - 1 - t * kBN - 4 * hh;
+        if (CAUSAL) lim = min(lim, i + koff - t * kBN - 4 * hh);
 #pragma unroll
         for (int k = 0; k < 64; ++k) {
-          const int key = t * kBN + 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * hh + (k & 3);
-          const bool vis = key < s.kv_len && (!CAUSAL || key <= i + koff);
-          x[k] = vis ? x[k] : kNegInf;
+          const int off = 32 * (k >> 4) + 8 * ((k & 15) >> 2) + (k & 3);
+          x[k] = off <= lim ? x[k] : kNegInf;
         }
       }
       // running max over the previous value and this tile's keys, then over the two half-waves
