@@ -104,9 +104,9 @@ __device__ inline void load_rows(uint4 (&v)[NROWS * D / 8 / 256], const void* ba
   }
 }
 
-// The same rows, raw, into LDS rows of D elements.
-template <int D, int NROWS>
-__device__ inline void stage_rows(uint16_t (*dst)[D], const void* base, const int64_t* strides, int b,
+// The same rows, raw, into LDS rows of P >= D elements.
+template <int D, int NROWS, int P = D>
+__device__ inline void stage_rows(uint16_t (*dst)[P], const void* base, const int64_t* strides, int b,
                                   int64_t tok0, int head, int n, int dt) {
   constexpr int RW = D / 8;
   uint4 v[NROWS * RW / 256];
@@ -266,15 +266,21 @@ __device__ inline void widen32(const uint16_t* p, float (&f)[32]) {
   }
 }
 
+// Row pitch (elements) of the Q and K rows that lanes then read 32 channels at a time: 16 bytes
+// more than a row, so the rows of consecutive keys start in different LDS banks (with a pitch of
+// exactly D the lanes of one channel group would all hit the same banks).
+template <int D>
+constexpr int kPitch = D + 8;
+
 // ---- Q: block mean, per-token INT4 codes -------------------------------------------------------
 // One workgroup of 256 per (Q block, q head, sequence). The block's rows are read once, coalesced,
 // into LDS (rows past the sequence end are zero and add +0.0 to the fp64 sums); thread c sums
 // channel c in row order. The rows are then quantized with D/32 lanes per row and 32 channels per
 // lane (one scale per token: on gfx950 a lane owns one query column of the S^T = K Q^T MFMA tile,
 // so the per-thread group is one token).
-// LDS bytes: the block's Q rows (kQBlock x D raw elements), then the D block means (f32)
+// LDS bytes: the block's Q rows (kQBlock rows of kPitch raw elements), then the D block means (f32)
 template <int D>
-constexpr int kQuantQLds = 2 * kQBlock * D + 4 * D;
+constexpr int kQuantQLds = 2 * kQBlock * kPitch<D> + 4 * D;
 
 template <int D, int IN>
 __device__ inline void quant_q_block(const KArgs& a, int qb, int h, int b, uint8_t* lds) {
@@ -282,9 +288,9 @@ __device__ inline void quant_q_block(const KArgs& a, int qb, int h, int b, uint8
   const Seq s = load_seq(a, b);
   if (qb * kQBlock >= s.q_len) return;
   const int i0 = qb * kQBlock, n = min(kQBlock, s.q_len - i0);
-  uint16_t(*rows)[D] = reinterpret_cast<uint16_t(*)[D]>(lds);
-  float* qbar = reinterpret_cast<float*>(lds + 2 * kQBlock * D);
-  stage_rows<D, kQBlock>(rows, a.q, a.qs, b, s.q_start + i0, h, n, a.dt);
+  uint16_t(*rows)[kPitch<D>] = reinterpret_cast<uint16_t(*)[kPitch<D>]>(lds);
+  float* qbar = reinterpret_cast<float*>(lds + 2 * kQBlock * kPitch<D>);
+  stage_rows<D, kQBlock, kPitch<D>>(rows, a.q, a.qs, b, s.q_start + i0, h, n, a.dt);
   __syncthreads();
   if (tid < D) {
     double sum = 0.0;
@@ -369,11 +375,11 @@ __global__ __launch_bounds__(256) void k_stats_quant_q(KArgs a, int n_chunks) {
 // the 16 keys of 32-key subtile w/2 whose index has bit 2 equal to w%2 (the keys one lane half
 // owns), D/32 lanes per key with 32 channels each; the smoothed values stay in registers between
 // the group max and the codes.
-// LDS bytes of one K/V quantizer workgroup: kbar, 1/s_v (D floats each), the K rows (kKVTile x D
-// raw elements), and the V codes in the output order (for channel c and lane half h the 32 fp8
-// bytes of the keys tile_key(h, 0..31), at byte 32 (2c + h))
+// LDS bytes of one K/V quantizer workgroup: kbar, 1/s_v (D floats each), the K rows (kKVTile rows
+// of kPitch raw elements), and the V codes in the output order (for channel c and lane half h the
+// 32 fp8 bytes of the keys tile_key(h, 0..31), at byte 32 (2c + h))
 template <int D>
-constexpr int kQuantKvLds = 8 * D + 2 * kKVTile * D + 64 * D;
+constexpr int kQuantKvLds = 8 * D + 2 * kKVTile * kPitch<D> + 64 * D;
 
 template <int D, int IN>
 __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_t* lds) {
@@ -383,15 +389,15 @@ __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_
   if (t * kKVTile >= kvpad) return;
   float* kbar = reinterpret_cast<float*>(lds);
   float* svinv = kbar + D;
-  uint16_t(*kr)[D] = reinterpret_cast<uint16_t(*)[D]>(lds + 8 * D);
-  uint32_t* vt8 = reinterpret_cast<uint32_t*>(lds + 8 * D + 2 * kKVTile * D);
+  uint16_t(*kr)[kPitch<D>] = reinterpret_cast<uint16_t(*)[kPitch<D>]>(lds + 8 * D);
+  uint32_t* vt8 = reinterpret_cast<uint32_t*>(lds + 8 * D + 2 * kKVTile * kPitch<D>);
   const int64_t sidx = ((int64_t)b * a.Hkv + g) * D;
   if (tid < D) {
     kbar[tid] = ws_ptr<float>(a, a.lay.kbar)[sidx + tid];
     svinv[tid] = ws_ptr<float>(a, a.lay.sv_inv)[sidx + tid];
   }
   const int n = max(0, min(kKVTile, s.kv_len - t * kKVTile));
-  stage_rows<D, kKVTile>(kr, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n, a.dt);
+  stage_rows<D, kKVTile, kPitch<D>>(kr, a.k, a.ks, b, s.kv_start + t * kKVTile, g, n, a.dt);
   // V: this thread's 16-byte chunk (channels 8 ch + [0, 8)) of KPT keys that are consecutive both
   // in the tile and in the output order (slots s0 .. s0 + KPT - 1 of lane half h)
   constexpr int RW = D / 8;
