@@ -377,9 +377,14 @@ __global__ __launch_bounds__(256) void k_stats_quant_q(KArgs a, int n_chunks) {
 // the group max and the codes.
 // LDS bytes of one K/V quantizer workgroup: kbar, 1/s_v (D floats each), the K rows (kKVTile rows
 // of kPitch raw elements), and the V codes in the output order (for channel c and lane half h the
-// 32 fp8 bytes of the keys tile_key(h, 0..31), at byte 32 (2c + h))
+// 32 fp8 bytes of the keys tile_key(h, 0..31), at byte vrow(c, h))
 template <int D>
-constexpr int kQuantKvLds = 8 * D + 2 * kKVTile * kPitch<D> + 64 * D;
+constexpr int kQuantKvLds = 8 * D + 2 * kKVTile * kPitch<D> + 64 * D + 2 * D;
+
+// Byte offset of the V code row of channel c, lane half h: rows of 32 bytes, with 16 more bytes
+// after every 8 channels, so that the words the lanes of one wave write for the same channel index
+// (channels 8 apart) fall in different LDS banks
+__device__ inline int vrow(int c, int h) { return (2 * c + h) * 32 + 16 * (c >> 3); }
 
 template <int D, int IN>
 __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_t* lds) {
@@ -425,9 +430,9 @@ __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_
       const float sc = svinv[c];
       const int w = cvt_fp8x2(f[0][i] * sc, f[1][i] * sc, 0, false);
       if constexpr (KPT == 4) {
-        vt8[((2 * c + h) * 32 + s0) / 4] = (uint32_t)cvt_fp8x2(f[2][i] * sc, f[3][i] * sc, w, true);
+        vt8[(vrow(c, h) + s0) / 4] = (uint32_t)cvt_fp8x2(f[2][i] * sc, f[3][i] * sc, w, true);
       } else {
-        reinterpret_cast<uint16_t*>(vt8)[((2 * c + h) * 32 + s0) / 2] = (uint16_t)w;
+        reinterpret_cast<uint16_t*>(vt8)[(vrow(c, h) + s0) / 2] = (uint16_t)w;
       }
     }
   }
@@ -470,7 +475,7 @@ __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_
   uint8_t* v8 = ws_ptr<uint8_t>(a, a.lay.v8) +
                 ((int64_t)g * (a.lay.kv_rows / kKVTile) + s.kv_row0 / kKVTile + t) * (kKVTile * D);
   for (int p = tid; p < 2 * D; p += 256) {
-    const uint4* src = reinterpret_cast<const uint4*>(vt8) + 2 * p;
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(vt8) + vrow(p >> 1, p & 1));
     uint4* dst = reinterpret_cast<uint4*>(v8 + (int64_t)p * 32);
     dst[0] = src[0];
     dst[1] = src[1];
