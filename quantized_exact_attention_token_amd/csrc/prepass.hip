@@ -503,6 +503,87 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 template <int D>
 constexpr int kDeltaLds = 4 * kKVTile * (D + 4);
 
+// What a correction-table work item needs besides its pair block and key range.
+struct DeltaItem {
+  const KArgs& a;
+  const Seq& s;
+  const float* kt;  // k~ tile in LDS, rows of D + 4 floats
+  const double* qbar64;
+  float* delta;
+  double L;
+  int t, g, grp, qbmin, nlive, koff, kvpad, li, lk;
+};
+
+// Correction values of 32 pairs (from p0) x 16 NKB keys (from key k0 of the tile): 2 x NKB fp64
+// MFMA tiles over all D channels, then the stores.
+template <int D, int NKB>
+__device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
+  constexpr int KS = D + 4;
+  const double* qrow[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int pc = min(p0 + 16 * rb + c.li, c.nlive - 1);
+    const int h = c.g * c.grp + pc % c.grp, qb = c.qbmin + pc / c.grp;
+    qrow[rb] = c.qbar64 + ((int64_t)h * c.a.lay.q_blocks + c.s.qblk0 + qb) * D + c.lk;
+  }
+  v4d acc[2][NKB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) acc[rb][kb] = v4d{0.0, 0.0, 0.0, 0.0};
+  // channels in chunks of 16 (4 MFMA k-steps); the next chunk's means are requested before the
+  // current chunk's MFMAs, so their latency hides behind them
+  // (rows of pairs past the end read the clamped last pair: an output row depends only on its
+  // own A row, and those rows are never stored)
+  double a_cur[4][2], a_nxt[4][2];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = qrow[rb][4 * u];
+  const float* kr = c.kt + (k0 + c.li) * KS + c.lk;
+#pragma unroll 1
+  for (int ch = 0; ch < D; ch += 16) {
+    const int nx = ch + 16 < D ? ch + 16 : 0;  // (the last prefetch rereads chunk 0, unused)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) a_nxt[u][rb] = qrow[rb][nx + 4 * u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      double bv[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) bv[kb] = (double)kr[16 * kb * KS + ch + 4 * u];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          acc[rb][kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a_cur[u][rb], bv[kb], acc[rb][kb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = a_nxt[u][rb];
+  }
+  // D[i][j]: pair p0 + 16 rb + lk + 4 r, key t*64 + k0 + 16 kb + li
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pair = p0 + 16 * rb + c.lk + 4 * r;
+      if (pair >= c.nlive) continue;
+      const int h = c.g * c.grp + pair % c.grp, qb = c.qbmin + pair / c.grp;
+      // last key that any row of Q block qb sees
+      int jm = c.s.kv_len - 1;
+      if (c.a.causal) jm = min(jm, min(c.s.q_len, (qb + 1) * kQBlock) - 1 + c.koff);
+      float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 + (int64_t)qb * c.kvpad;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int j = c.t * kKVTile + k0 + 16 * kb + c.li;
+        drow[j] = j <= jm ? (float)(acc[rb][kb][r] * c.L) : 0.0f;
+      }
+    }
+}
+
 template <int D, int IN>
 __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt) {
   constexpr int KS = D + 4;  // floats per k~ row in LDS
@@ -535,13 +616,7 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   const double L = (double)a.L;
   float* delta = ws_ptr<float>(a, a.lay.delta);
   const double* qbar64 = ws_ptr<double>(a, a.lay.qbar64);
-  // last key that any row of Q block qb sees
-  auto jmax_of = [&](int qb) {
-    int jm = s.kv_len - 1;
-    if (a.causal) jm = min(jm, min(s.q_len, (qb + 1) * kQBlock) - 1 + koff);
-    return jm;
-  };
-  // first Q block that sees a key of this tile (jmax_of is non-decreasing in qb)
+  // first Q block that sees a key of this tile (the last key a Q block sees is non-decreasing in qb)
   int qbmin;
   if (t * kKVTile >= s.kv_len) {
     qbmin = nqb;
@@ -551,71 +626,17 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
     const int T = t * kKVTile + 1 - koff;  // needs min(q_len, (qb + 1) * 128) >= T
     qbmin = T <= 0 ? 0 : (T > s.q_len ? nqb : (T + kQBlock - 1) / kQBlock - 1);
   }
-  // live pairs, Q-block major: pair p -> Q block qbmin + p / grp, q head g * grp + p % grp;
-  // blocks of 32 pairs go round-robin to the waves
+  // live pairs, Q-block major: pair p -> Q block qbmin + p / grp, q head g * grp + p % grp. Work
+  // items are blocks of 32 pairs x the tile's 64 keys, dealt round-robin to the waves; a tile with
+  // fewer than 4 blocks (one or two q heads per kv head, or the last tiles under a causal mask)
+  // splits each block's keys in two halves instead, so that up to twice as many waves have work
   const int nlive = (nqb - qbmin) * grp;
-  for (int p0 = 32 * wave; p0 < nlive; p0 += 128) {
-    const double* qrow[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int pc = min(p0 + 16 * rb + li, nlive - 1);
-      const int h = g * grp + pc % grp, qb = qbmin + pc / grp;
-      qrow[rb] = qbar64 + ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + lk;
-    }
-    v4d acc[2][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc[rb][kb] = v4d{0.0, 0.0, 0.0, 0.0};
-    // channels in chunks of 16 (4 MFMA k-steps); the next chunk's means are requested before the
-    // current chunk's MFMAs, so their latency hides behind 32 MFMAs
-    // (rows of pairs past the end read the clamped last pair: an output row depends only on its
-    // own A row, and those rows are never stored)
-    double a_cur[4][2], a_nxt[4][2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = qrow[rb][4 * u];
-    const float* kr = kt + li * KS + lk;
-#pragma unroll 1
-    for (int ch = 0; ch < D; ch += 16) {
-      const int nx = ch + 16 < D ? ch + 16 : 0;  // (the last prefetch rereads chunk 0, unused)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) a_nxt[u][rb] = qrow[rb][nx + 4 * u];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        double bv[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) bv[kb] = (double)kr[16 * kb * KS + ch + 4 * u];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            acc[rb][kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a_cur[u][rb], bv[kb], acc[rb][kb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = a_nxt[u][rb];
-    }
-    // D[i][j]: pair p0 + 16 rb + lk + 4 r, key t*64 + 16 kb + li
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pair = p0 + 16 * rb + lk + 4 * r;
-        if (pair >= nlive) continue;
-        const int h = g * grp + pair % grp, qb = qbmin + pair / grp;
-        const int jm = jmax_of(qb);
-        float* drow = delta + (int64_t)h * a.lay.delta_len + s.delta0 + (int64_t)qb * kvpad;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int j = t * kKVTile + 16 * kb + li;
-          drow[j] = j <= jm ? (float)(acc[rb][kb][r] * L) : 0.0f;
-        }
-      }
+  const int nblk = (nlive + 31) / 32;
+  const DeltaItem it{a, s, kt, qbar64, delta, L, t, g, grp, qbmin, nlive, koff, kvpad, li, lk};
+  if (nblk >= 4) {
+    for (int w = wave; w < nblk; w += 4) delta_item<D, 4>(it, 32 * w, 0);
+  } else {
+    for (int w = wave; w < 2 * nblk; w += 4) delta_item<D, 2>(it, 32 * (w >> 1), 32 * (w & 1));
   }
 }
 
