@@ -109,7 +109,6 @@ typedef struct {
  *   kbar       f32   [B][H_kv][d]             K channel means
  *   sv, sv_inv f32   [B][H_kv][d]             V channel scale amax/448 and its inverse 448/amax
  *   qbar       f32   [H_q][q_blocks][d]       Q block means
- *   qbar64     f64   [H_q][q_blocks][d]       the same means widened to fp64 (read by the pre-pass)
  *   qcode      u8    [H_q][q_rows][3d/4]      INT4 codes in 6-bit e2m3 fields (the gfx950 fp6
  *                                             MFMA operand format, exact for -7..7): channel c at
  *                                             bits [6c, 6c+6) of the row, little-endian
@@ -127,7 +126,7 @@ typedef struct {
 typedef struct {
   int64_t total_bytes;
   int64_t q_rows, kv_rows, q_blocks, delta_len;  /* per head, summed over sequences */
-  int64_t seq_table, k_partial, v_partial, kbar, sv, sv_inv, qbar, qbar64, qcode, sq, kcode, sk, v8,
+  int64_t seq_table, k_partial, v_partial, kbar, sv, sv_inv, qbar, qcode, sq, kcode, sk, v8,
       delta;
 } sage2_ws_layout;
 

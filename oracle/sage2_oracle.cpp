@@ -261,15 +261,17 @@ int orc_quantize(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int fl
         sq[(size_t)h * Lq + i] = s.s;
         for (int c = 0; c < d; ++c) qcode[((size_t)h * Lq + i) * d + c] = int4_code(qt[c], s.inv);
       }
-      // 5. Correction term: the block mean's exact contribution q̄·k̃_j, which the smoothed
-      //    INT4 product leaves out. fp64 fused multiply-add chain in channel order, scaled to
-      //    base-2 logit units (times sm_scale*log2 e) and rounded once to f32.
+      // 5. Correction term: the block mean's contribution q̄·k̃_j with the unquantized smoothed
+      //    K, which the smoothed INT4 product leaves out. The pages fix no precision for it; it
+      //    is taken in f32 like every other float of the path: a fused multiply-add chain over
+      //    the channels in order, starting from +0, then scaled to base-2 logit units (one f32
+      //    multiply by sm_scale*log2 e).
       if (delta) {
         float* D = delta + ((size_t)h * nqb + b) * Lkv;
         for (int j = 0; j < Lkv; ++j) {
-          double acc = 0.0;
-          for (int c = 0; c < d; ++c) acc = std::fma((double)qb[c], (double)KT[(size_t)j * d + c], acc);
-          D[j] = (float)(acc * (double)L);
+          float acc = 0.0f;
+          for (int c = 0; c < d; ++c) acc = std::fmaf(qb[c], KT[(size_t)j * d + c], acc);
+          D[j] = acc * L;
         }
       }
     }

@@ -46,7 +46,7 @@ class Params(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_bytes", "q_rows", "kv_rows", "q_blocks", "delta_len", "seq_table", "k_partial",
-        "v_partial", "kbar", "sv", "sv_inv", "qbar", "qbar64", "qcode", "sq", "kcode", "sk", "v8",
+        "v_partial", "kbar", "sv", "sv_inv", "qbar", "qcode", "sq", "kcode", "sk", "v8",
         "delta")]
 
 

@@ -109,7 +109,6 @@ void compute_layout(const sage2_params* p, sage2_ws_layout* L) {
   L->sv = take((int64_t)p->B * p->H_kv * d * 4);
   L->sv_inv = take((int64_t)p->B * p->H_kv * d * 4);
   L->qbar = take(p->H_q * L->q_blocks * d * 4);
-  L->qbar64 = take(p->H_q * L->q_blocks * d * 8);
   L->qcode = take(p->H_q * L->q_rows * d * 3 / 4);
   L->sq = take(p->H_q * L->q_rows * 4);
   L->kcode = take(p->H_kv * L->kv_rows * d * 3 / 4);

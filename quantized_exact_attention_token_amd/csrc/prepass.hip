@@ -300,7 +300,6 @@ __device__ inline void quant_q_block(const KArgs& a, int qb, int h, int b, uint8
     qbar[tid] = m;
     const int64_t at = ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + tid;
     ws_ptr<float>(a, a.lay.qbar)[at] = m;
-    ws_ptr<double>(a, a.lay.qbar64)[at] = (double)m;
   }
   __syncthreads();
   uint8_t* qcode = ws_ptr<uint8_t>(a, a.lay.qcode);
@@ -483,13 +482,15 @@ __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_
 }
 
 // ---- correction table: delta[qb][j] = (qbar_qb . ktilde_j) * sm_scale * log2(e) ---------------
-// Q smoothing removes each block's mean from the INT4 product; this adds back its exact share:
-// an fp64 fused multiply-add chain over the channels in order, scaled and rounded once to f32.
-// The chains run on v_mfma_f64_16x16x4_f64: on gfx950 it accumulates every output as four fused
-// multiply-adds in k order on top of C (checked bit for bit against sequential fma() on
-// cancellation-heavy inputs), so feeding it the channels four at a time, in order, is exactly
-// the channel-order chain. Operand layouts: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k,
-// D[i][j] in lane j + 16 (i % 4), register i / 4.
+// Q smoothing removes each block's mean from the INT4 product; this adds back its share with the
+// unquantized smoothed K: an f32 fused multiply-add chain over the channels in order from +0,
+// then one f32 multiply by sm_scale * log2(e).
+// The chains run on v_mfma_f32_16x16x4_f32: on gfx950 it accumulates every output as four fused
+// multiply-adds in k order on top of C (checked bit for bit against sequential fmaf() on
+// 4.2 million outputs of random-sign inputs spread over 24 binades), so feeding it the channels
+// four at a time, in order, is exactly the channel-order chain, at twice the fp64 MFMA's rate.
+// Operand layouts: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane
+// j + 16 (i / 4), register i % 4.
 // One workgroup of 256 per (64-key tile, kv head, sequence): k~ of the tile in LDS (f32, a 4-float
 // row skew). Only the (q head, Q block) pairs that see a key of the tile are computed: they are
 // numbered Q block major and dealt to the waves in blocks of 32 pairs x the 64 keys = 2 x 4 MFMA
@@ -497,7 +498,7 @@ __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_
 // block are left unwritten (the attention kernel masks such keys by selection, never reads them
 // into arithmetic that reaches the output) except within a computed tile, where they are stored as
 // 0.
-typedef double v4d __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // LDS bytes of one correction-table workgroup: the tile's k~ rows of D + 4 floats
 template <int D>
@@ -508,34 +509,34 @@ struct DeltaItem {
   const KArgs& a;
   const Seq& s;
   const float* kt;  // k~ tile in LDS, rows of D + 4 floats
-  const double* qbar64;
+  const float* qbar;
   float* delta;
-  double L;
+  float L;
   int t, g, grp, qbmin, nlive, koff, kvpad, li, lk;
 };
 
-// Correction values of 32 pairs (from p0) x 16 NKB keys (from key k0 of the tile): 2 x NKB fp64
+// Correction values of 32 pairs (from p0) x 16 NKB keys (from key k0 of the tile): 2 x NKB f32
 // MFMA tiles over all D channels, then the stores.
 template <int D, int NKB>
 __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
   constexpr int KS = D + 4;
-  const double* qrow[2];
+  const float* qrow[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int pc = min(p0 + 16 * rb + c.li, c.nlive - 1);
     const int h = c.g * c.grp + pc % c.grp, qb = c.qbmin + pc / c.grp;
-    qrow[rb] = c.qbar64 + ((int64_t)h * c.a.lay.q_blocks + c.s.qblk0 + qb) * D + c.lk;
+    qrow[rb] = c.qbar + ((int64_t)h * c.a.lay.q_blocks + c.s.qblk0 + qb) * D + c.lk;
   }
-  v4d acc[2][NKB];
+  v4f acc[2][NKB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) acc[rb][kb] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int kb = 0; kb < NKB; ++kb) acc[rb][kb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   // channels in chunks of 16 (4 MFMA k-steps); the next chunk's means are requested before the
   // current chunk's MFMAs, so their latency hides behind them
   // (rows of pairs past the end read the clamped last pair: an output row depends only on its
   // own A row, and those rows are never stored)
-  double a_cur[4][2], a_nxt[4][2];
+  float a_cur[4][2], a_nxt[4][2];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -550,26 +551,26 @@ __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
       for (int rb = 0; rb < 2; ++rb) a_nxt[u][rb] = qrow[rb][nx + 4 * u];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      double bv[NKB];
+      float bv[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) bv[kb] = (double)kr[16 * kb * KS + ch + 4 * u];
+      for (int kb = 0; kb < NKB; ++kb) bv[kb] = kr[16 * kb * KS + ch + 4 * u];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          acc[rb][kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a_cur[u][rb], bv[kb], acc[rb][kb], 0, 0, 0);
+          acc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[u][rb], bv[kb], acc[rb][kb], 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = a_nxt[u][rb];
   }
-  // D[i][j]: pair p0 + 16 rb + lk + 4 r, key t*64 + k0 + 16 kb + li
+  // D[i][j]: pair p0 + 16 rb + 4 lk + r, key t*64 + k0 + 16 kb + li
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int pair = p0 + 16 * rb + c.lk + 4 * r;
+      const int pair = p0 + 16 * rb + 4 * c.lk + r;
       if (pair >= c.nlive) continue;
       const int h = c.g * c.grp + pair % c.grp, qb = c.qbmin + pair / c.grp;
       // last key that any row of Q block qb sees
@@ -579,7 +580,7 @@ __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int j = c.t * kKVTile + k0 + 16 * kb + c.li;
-        drow[j] = j <= jm ? (float)(acc[rb][kb][r] * c.L) : 0.0f;
+        drow[j] = j <= jm ? acc[rb][kb][r] * c.L : 0.0f;
       }
     }
 }
@@ -613,9 +614,8 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   const int nqb = (s.q_len + kQBlock - 1) / kQBlock;
   const int koff = s.kv_len - s.q_len;
   const int li = lane & 15, lk = lane >> 4;
-  const double L = (double)a.L;
   float* delta = ws_ptr<float>(a, a.lay.delta);
-  const double* qbar64 = ws_ptr<double>(a, a.lay.qbar64);
+  const float* qbar = ws_ptr<float>(a, a.lay.qbar);
   // first Q block that sees a key of this tile (the last key a Q block sees is non-decreasing in qb)
   int qbmin;
   if (t * kKVTile >= s.kv_len) {
@@ -632,7 +632,7 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   // splits each block's keys in two halves instead, so that up to twice as many waves have work
   const int nlive = (nqb - qbmin) * grp;
   const int nblk = (nlive + 31) / 32;
-  const DeltaItem it{a, s, kt, qbar64, delta, L, t, g, grp, qbmin, nlive, koff, kvpad, li, lk};
+  const DeltaItem it{a, s, kt, qbar, delta, a.L, t, g, grp, qbmin, nlive, koff, kvpad, li, lk};
   if (nblk >= 4) {
     for (int w = wave; w < nblk; w += 4) delta_item<D, 4>(it, 32 * w, 0);
   } else {

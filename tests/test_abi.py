@@ -54,7 +54,7 @@ def test_workspace_size_closed_form(lib):
     assert (lay.q_rows, lay.kv_rows, lay.q_blocks, lay.delta_len) == (768, 1024, 6, 2 * 3 * 512)
     assert n >= 8 * 768 * 64 + 2 * 1024 * 64 + 2 * 1024 * 128 + 8 * 3072 * 4
     offs = [lay.seq_table, lay.k_partial, lay.v_partial, lay.kbar, lay.sv, lay.sv_inv, lay.qbar,
-            lay.qbar64, lay.qcode, lay.sq, lay.kcode, lay.sk, lay.v8, lay.delta]
+            lay.qcode, lay.sq, lay.kcode, lay.sk, lay.v8, lay.delta]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.delta + 8 * lay.delta_len * 4 <= n
 

@@ -284,15 +284,28 @@ def test_q_correction_restores_logits():
 
 
 def test_delta_is_mean_times_smoothed_k():
-    """The stored correction equals L·(q̄·k̃) computed with numpy's fp64 matmul (library routine),
-    within the single f32 rounding."""
+    """The stored correction equals L·(q̄·k̃), k̃ = f32(k - k̄), computed with numpy's fp64 matmul
+    (library routine), within the error bound of an f32 multiply-add chain over d channels
+    (gamma_d = d u / (1 - d u), u = 2^-24, times sum_c |q̄_c k̃_c|) plus the final f32 multiply's
+    rounding. A dropped, repeated or sign-flipped channel term is far outside that bound."""
     w = W.custom(1, 4, 2, 300, 200, 64, torch.float16, seed=9, q_offset_std=2.0)
     q, k, v = _seq(w)
     z = O.quantize(q, k, v)
-    kt = (k - z.kbar[:, None, :]).astype(np.float64)
-    ref = np.einsum("hbd,hjd->hbj", z.qbar.astype(np.float64), np.repeat(kt, 2, axis=0))
-    ref *= float(_L(64))
-    assert np.max(np.abs(z.delta - ref) / (np.abs(ref) + 1e-30)) <= 2 ** -23
+    kt = (k - z.kbar[:, None, :]).astype(np.float32).astype(np.float64)
+    qb = z.qbar.astype(np.float64)
+    ktr = np.repeat(kt, 2, axis=0)
+    L = float(_L(64))
+    ref = np.einsum("hbd,hjd->hbj", qb, ktr) * L
+    sabs = np.einsum("hbd,hjd->hbj", np.abs(qb), np.abs(ktr)) * L
+    u = 2.0 ** -24
+    gamma = 64 * u / (1 - 64 * u)
+    bound = gamma * sabs * (1 + u) + u * np.abs(ref) + 1e-30
+    err = np.abs(z.delta.astype(np.float64) - ref)
+    assert np.all(err <= bound)
+    # the bound is tight enough to see one channel term: every |q̄_c k̃_c| of a random input is
+    # larger than the allowed error for most entries
+    one_term = np.abs(qb[:, :, :1]) * np.abs(ktr[:, None, :, 0]) * L
+    assert np.mean(one_term > bound) > 0.9
 
 
 def test_logits_within_int4_error_bound():
