@@ -75,6 +75,11 @@ __device__ inline void widen8(const uint4 v, float (&f)[8]) {
   }
 }
 
+// Position of channel c in a row of the correction MFMA's operands (the block means in the
+// workspace, the smoothed K tile in LDS): within each 16-channel group, the channels c, c+4, c+8,
+// c+12 that one lane feeds to four consecutive k-steps sit side by side.
+__device__ constexpr int mma_pos(int c) { return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3); }
+
 // Rows [tok0, tok0 + n) of one head of a strided input, as 16-byte chunks for a block of 256
 // threads: chunk k of thread x is row (x + 256 k) / (D/8), channels 8 ((x + 256 k) % (D/8)) + [0, 8).
 // All of a thread's loads are issued before any is waited on; rows n..NROWS-1 and channels dt..D-1
@@ -298,7 +303,7 @@ __device__ inline void quant_q_block(const KArgs& a, int qb, int h, int b, uint8
     for (int i = 0; i < kQBlock; ++i) sum += (double)widen16<IN>(rows[i][tid]);
     const float m = (a.flags & SAGE2_NO_Q_SMOOTH) ? 0.0f : (float)(sum / (double)n);
     qbar[tid] = m;
-    const int64_t at = ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + tid;
+    const int64_t at = ((int64_t)h * a.lay.q_blocks + s.qblk0 + qb) * D + mma_pos(tid);
     ws_ptr<float>(a, a.lay.qbar)[at] = m;
   }
   __syncthreads();
@@ -492,7 +497,7 @@ __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_
 // Operand layouts: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane
 // j + 16 (i / 4), register i % 4.
 // One workgroup of 256 per (64-key tile, kv head, sequence): k~ of the tile in LDS (f32, a 4-float
-// row skew). Only the (q head, Q block) pairs that see a key of the tile are computed: they are
+// row skew, channels in MFMA order). Only the (q head, Q block) pairs that see a key of the tile are computed: they are
 // numbered Q block major and dealt to the waves in blocks of 32 pairs x the 64 keys = 2 x 4 MFMA
 // tiles, so a causal mask leaves no wave idle. Entries a causal mask hides from every row of a Q
 // block are left unwritten (the attention kernel masks such keys by selection, never reads them
@@ -525,45 +530,39 @@ __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
   for (int rb = 0; rb < 2; ++rb) {
     const int pc = min(p0 + 16 * rb + c.li, c.nlive - 1);
     const int h = c.g * c.grp + pc % c.grp, qb = c.qbmin + pc / c.grp;
-    qrow[rb] = c.qbar + ((int64_t)h * c.a.lay.q_blocks + c.s.qblk0 + qb) * D + c.lk;
+    qrow[rb] = c.qbar + ((int64_t)h * c.a.lay.q_blocks + c.s.qblk0 + qb) * D + 4 * c.lk;
   }
   v4f acc[2][NKB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) acc[rb][kb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  // channels in chunks of 16 (4 MFMA k-steps); the next chunk's means are requested before the
-  // current chunk's MFMAs, so their latency hides behind them
-  // (rows of pairs past the end read the clamped last pair: an output row depends only on its
-  // own A row, and those rows are never stored)
-  float a_cur[4][2], a_nxt[4][2];
+  // channels in chunks of 16 (4 MFMA k-steps). Both operands are stored with the channels of a
+  // chunk in MFMA order (mma_pos), so one 16-byte read gives a lane its operand for all 4 k-steps.
+  // The next chunk's means are requested before the current chunk's MFMAs, so their latency hides
+  // behind them (rows of pairs past the end read the clamped last pair: an output row depends
+  // only on its own A row, and those rows are never stored)
+  v4f a_cur[2], a_nxt[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = qrow[rb][4 * u];
-  const float* kr = c.kt + (k0 + c.li) * KS + c.lk;
+  for (int rb = 0; rb < 2; ++rb) a_cur[rb] = *reinterpret_cast<const v4f*>(qrow[rb]);
+  const float* kr = c.kt + (k0 + c.li) * KS + 4 * c.lk;
 #pragma unroll 1
   for (int ch = 0; ch < D; ch += 16) {
     const int nx = ch + 16 < D ? ch + 16 : 0;  // (the last prefetch rereads chunk 0, unused)
 #pragma unroll
+    for (int rb = 0; rb < 2; ++rb) a_nxt[rb] = *reinterpret_cast<const v4f*>(qrow[rb] + nx);
+    v4f bv[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) bv[kb] = *reinterpret_cast<const v4f*>(kr + 16 * kb * KS + ch);
+#pragma unroll
     for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a_nxt[u][rb] = qrow[rb][nx + 4 * u];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float bv[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) bv[kb] = kr[16 * kb * KS + ch + 4 * u];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          acc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[u][rb], bv[kb], acc[rb][kb], 0, 0, 0);
-    }
+          acc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[rb][u], bv[kb][u], acc[rb][kb], 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a_cur[u][rb] = a_nxt[u][rb];
+    for (int rb = 0; rb < 2; ++rb) a_cur[rb] = a_nxt[rb];
   }
   // D[i][j]: pair p0 + 16 rb + 4 lk + r, key t*64 + k0 + 16 kb + li
 #pragma unroll
@@ -606,7 +605,7 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
       float f[8];
       widen8<IN>(v[k], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kt[key * KS + 8 * ch + e] = key < n ? f[e] - kbar[8 * ch + e] : 0.0f;
+      for (int e = 0; e < 8; ++e) kt[key * KS + mma_pos(8 * ch + e)] = key < n ? f[e] - kbar[8 * ch + e] : 0.0f;
     }
   }
   __syncthreads();
