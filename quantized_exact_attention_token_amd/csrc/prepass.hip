@@ -551,6 +551,9 @@ __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
     const int nx = ch + 16 < D ? ch + 16 : 0;  // (the last prefetch rereads chunk 0, unused)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) a_nxt[rb] = *reinterpret_cast<const v4f*>(qrow[rb] + nx);
+    // (an empty asm statement that clobbers memory keeps these loads in this iteration: without
+    // it the compiler moves them into the next one, next to their use, and waits on them there)
+    asm volatile("" ::: "memory");
     v4f bv[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) bv[kb] = *reinterpret_cast<const v4f*>(kr + 16 * kb * KS + ch);
