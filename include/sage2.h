@@ -108,8 +108,8 @@ typedef struct {
  *   v_partial  f32   [H_kv][kv_rows/128][d]   per-128-token max |V|
  *   kbar       f32   [B][H_kv][d]             K channel means
  *   sv, sv_inv f32   [B][H_kv][d]             V channel scale amax/448 and its inverse 448/amax
- *   qbar       f32   [H_q][q_blocks][d]       Q block means; within each 16-channel group channel
- *                                             c sits at 4*(c%4) + (c%16)/4 (the order in which the
+ *   qbar       f32   [H_q][q_blocks][d]       Q block means; within each 8-channel group channel
+ *                                             c sits at 4*(c%2) + (c%8)/2 (the order in which the
  *                                             correction MFMA consumes them)
  *   qcode      u8    [H_q][q_rows][3d/4]      INT4 codes in 6-bit e2m3 fields (the gfx950 fp6
  *                                             MFMA operand format, exact for -7..7): channel c at

@@ -76,9 +76,9 @@ __device__ inline void widen8(const uint4 v, float (&f)[8]) {
 }
 
 // Position of channel c in a row of the correction MFMA's operands (the block means in the
-// workspace, the smoothed K tile in LDS): within each 16-channel group, the channels c, c+4, c+8,
-// c+12 that one lane feeds to four consecutive k-steps sit side by side.
-__device__ constexpr int mma_pos(int c) { return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3); }
+// workspace, the smoothed K tile in LDS): within each 8-channel group, the channels c, c+2, c+4,
+// c+6 that one lane feeds to four consecutive k-steps sit side by side.
+__device__ constexpr int mma_pos(int c) { return (c & ~7) | ((c & 1) << 2) | ((c >> 1) & 3); }
 
 // Rows [tok0, tok0 + n) of one head of a strided input, as 16-byte chunks for a block of 256
 // threads: chunk k of thread x is row (x + 256 k) / (D/8), channels 8 ((x + 256 k) % (D/8)) + [0, 8).
@@ -490,16 +490,16 @@ __device__ inline void quant_kv_tile(const KArgs& a, int t, int g, int b, uint8_
 // Q smoothing removes each block's mean from the INT4 product; this adds back its share with the
 // unquantized smoothed K: an f32 fused multiply-add chain over the channels in order from +0,
 // then one f32 multiply by sm_scale * log2(e).
-// The chains run on v_mfma_f32_16x16x4_f32: on gfx950 it accumulates every output as four fused
+// The chains run on v_mfma_f32_32x32x2_f32: on gfx950 it accumulates every output as two fused
 // multiply-adds in k order on top of C (checked bit for bit against sequential fmaf() on
-// 4.2 million outputs of random-sign inputs spread over 24 binades), so feeding it the channels
-// four at a time, in order, is exactly the channel-order chain, at twice the fp64 MFMA's rate.
-// Operand layouts: A[i][k] in lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane
-// j + 16 (i / 4), register i % 4.
+// 8.4 million outputs of random-sign inputs spread over 24 binades), so feeding it the channels
+// two at a time, in order, is exactly the channel-order chain, at twice the fp64 MFMA's rate.
+// Operand layouts: A[i][k] in lane i + 32k, B[k][j] in lane j + 32k, D[i][j] in lane
+// j + 32 ((i / 4) % 2), register 4 (i / 8) + i % 4.
 // One workgroup of 256 per (64-key tile, kv head, sequence): k~ of the tile in LDS (f32, a 4-float
-// row skew, channels in MFMA order). Only the (q head, Q block) pairs that see a key of the tile are computed: they are
-// numbered Q block major and dealt to the waves in blocks of 32 pairs x the 64 keys = 2 x 4 MFMA
-// tiles, so a causal mask leaves no wave idle. Entries a causal mask hides from every row of a Q
+// row skew, channels in MFMA order). Only the (q head, Q block) pairs that see a key of the tile
+// are computed: they are numbered Q block major and dealt to the waves in blocks of 32 pairs x the
+// 64 keys = 2 MFMA tiles, so a causal mask leaves no wave idle. Entries a causal mask hides from every row of a Q
 // block are left unwritten (the attention kernel masks such keys by selection, never reads them
 // into arithmetic that reaches the output) except within a computed tile, where they are stored as
 // 0.
@@ -520,71 +520,62 @@ struct DeltaItem {
   int t, g, grp, qbmin, nlive, koff, kvpad, li, lk;
 };
 
-// Correction values of 32 pairs (from p0) x 16 NKB keys (from key k0 of the tile): 2 x NKB f32
-// MFMA tiles over all D channels, then the stores.
+// Correction values of 32 pairs (from p0) x 32 NKB keys (from key k0 of the tile): NKB f32 MFMA
+// tiles of 32 x 32 over all D channels, then the stores.
 template <int D, int NKB>
 __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
   constexpr int KS = D + 4;
-  const float* qrow[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int pc = min(p0 + 16 * rb + c.li, c.nlive - 1);
+  // A[i][k]: the mean of pair p0 + i (rows of pairs past the end read the clamped last pair: an
+  // output row depends only on its own A row, and those rows are never stored)
+  const float* qrow;
+  {
+    const int pc = min(p0 + c.li, c.nlive - 1);
     const int h = c.g * c.grp + pc % c.grp, qb = c.qbmin + pc / c.grp;
-    qrow[rb] = c.qbar + ((int64_t)h * c.a.lay.q_blocks + c.s.qblk0 + qb) * D + 4 * c.lk;
+    qrow = c.qbar + ((int64_t)h * c.a.lay.q_blocks + c.s.qblk0 + qb) * D + 4 * c.lk;
   }
-  v4f acc[2][NKB];
+  v16f acc[NKB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) acc[rb][kb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  // channels in chunks of 16 (4 MFMA k-steps). Both operands are stored with the channels of a
-  // chunk in MFMA order (mma_pos), so one 16-byte read gives a lane its operand for all 4 k-steps.
-  // The next chunk's means are requested before the current chunk's MFMAs, so their latency hides
-  // behind them (rows of pairs past the end read the clamped last pair: an output row depends
-  // only on its own A row, and those rows are never stored)
-  v4f a_cur[2], a_nxt[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) a_cur[rb] = *reinterpret_cast<const v4f*>(qrow[rb]);
+  for (int kb = 0; kb < NKB; ++kb) acc[kb] = v16f{};
+  // channels in chunks of 8 (4 MFMA k-steps of 2 channels). Both operands are stored with the
+  // channels of a chunk in MFMA order (mma_pos), so one 16-byte read gives a lane its operand for
+  // all 4 k-steps. The next chunk's means are requested before the current chunk's MFMAs, so their
+  // latency hides behind them.
+  v4f a_cur = *reinterpret_cast<const v4f*>(qrow), a_nxt;
   const float* kr = c.kt + (k0 + c.li) * KS + 4 * c.lk;
 #pragma unroll 1
-  for (int ch = 0; ch < D; ch += 16) {
-    const int nx = ch + 16 < D ? ch + 16 : 0;  // (the last prefetch rereads chunk 0, unused)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) a_nxt[rb] = *reinterpret_cast<const v4f*>(qrow[rb] + nx);
-    // (an empty asm statement that clobbers memory keeps these loads in this iteration: without
-    // it the compiler moves them into the next one, next to their use, and waits on them there)
+  for (int ch = 0; ch < D; ch += 8) {
+    const int nx = ch + 8 < D ? ch + 8 : 0;  // (the last prefetch rereads chunk 0, unused)
+    a_nxt = *reinterpret_cast<const v4f*>(qrow + nx);
+    // (an empty asm statement that clobbers memory keeps this load in this iteration: without it
+    // the compiler moves it into the next one, next to its use, and waits on it there)
     asm volatile("" ::: "memory");
     v4f bv[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) bv[kb] = *reinterpret_cast<const v4f*>(kr + 16 * kb * KS + ch);
+    for (int kb = 0; kb < NKB; ++kb) bv[kb] = *reinterpret_cast<const v4f*>(kr + 32 * kb * KS + ch);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          acc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a_cur[rb][u], bv[kb][u], acc[rb][kb], 0, 0, 0);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) a_cur[rb] = a_nxt[rb];
+      for (int kb = 0; kb < NKB; ++kb)
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a_cur[u], bv[kb][u], acc[kb], 0, 0, 0);
+    a_cur = a_nxt;
   }
-  // D[i][j]: pair p0 + 16 rb + 4 lk + r, key t*64 + k0 + 16 kb + li
+  // D[i][j] in register r of lane l: pair p0 + 8 (r / 4) + 4 (l / 32) + r % 4, key
+  // t*64 + k0 + 32 kb + l % 32. One store instruction writes two pairs' 32 consecutive keys.
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int r = 0; r < 16; ++r) {
+    const int pair = p0 + 8 * (r >> 2) + 4 * c.lk + (r & 3);
+    if (pair >= c.nlive) continue;
+    const int h = c.g * c.grp + pair % c.grp, qb = c.qbmin + pair / c.grp;
+    // last key that any row of Q block qb sees
+    int jm = c.s.kv_len - 1;
+    if (c.a.causal) jm = min(jm, min(c.s.q_len, (qb + 1) * kQBlock) - 1 + c.koff);
+    float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 + (int64_t)qb * c.kvpad;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pair = p0 + 16 * rb + 4 * c.lk + r;
-      if (pair >= c.nlive) continue;
-      const int h = c.g * c.grp + pair % c.grp, qb = c.qbmin + pair / c.grp;
-      // last key that any row of Q block qb sees
-      int jm = c.s.kv_len - 1;
-      if (c.a.causal) jm = min(jm, min(c.s.q_len, (qb + 1) * kQBlock) - 1 + c.koff);
-      float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 + (int64_t)qb * c.kvpad;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int j = c.t * kKVTile + k0 + 16 * kb + c.li;
-        drow[j] = j <= jm ? acc[rb][kb][r] * c.L : 0.0f;
-      }
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int j = c.t * kKVTile + k0 + 32 * kb + c.li;
+      drow[j] = j <= jm ? acc[kb][r] * c.L : 0.0f;
     }
+  }
 }
 
 template <int D, int IN>
@@ -615,7 +606,7 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   const int grp = a.Hq / a.Hkv;
   const int nqb = (s.q_len + kQBlock - 1) / kQBlock;
   const int koff = s.kv_len - s.q_len;
-  const int li = lane & 15, lk = lane >> 4;
+  const int li = lane & 31, lk = lane >> 5;
   float* delta = ws_ptr<float>(a, a.lay.delta);
   const float* qbar = ws_ptr<float>(a, a.lay.qbar);
   // first Q block that sees a key of this tile (the last key a Q block sees is non-decreasing in qb)
@@ -636,9 +627,9 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   const int nblk = (nlive + 31) / 32;
   const DeltaItem it{a, s, kt, qbar, delta, a.L, t, g, grp, qbmin, nlive, koff, kvpad, li, lk};
   if (nblk >= 4) {
-    for (int w = wave; w < nblk; w += 4) delta_item<D, 4>(it, 32 * w, 0);
+    for (int w = wave; w < nblk; w += 4) delta_item<D, 2>(it, 32 * w, 0);
   } else {
-    for (int w = wave; w < 2 * nblk; w += 4) delta_item<D, 2>(it, 32 * (w >> 1), 32 * (w & 1));
+    for (int w = wave; w < 2 * nblk; w += 4) delta_item<D, 1>(it, 32 * (w >> 1), 32 * (w & 1));
   }
 }
 

@@ -103,9 +103,9 @@ class GpuRun:
         out["kbar"] = arr(lay.kbar, np.float32, self.p.B * Hkv * d).reshape(self.p.B, Hkv, d)[b]
         out["sv"] = arr(lay.sv, np.float32, self.p.B * Hkv * d).reshape(self.p.B, Hkv, d)[b]
         qbar = arr(lay.qbar, np.float32, Hq * lay.q_blocks * d).reshape(Hq, lay.q_blocks, d)
-        # stored in MFMA order within each 16-channel group: channel c at 4*(c%4) + (c%16)/4
+        # stored in MFMA order within each 8-channel group: channel c at 4*(c%2) + (c%8)/2
         cc = np.arange(d)
-        out["qbar"] = qbar[:, qblk0:qblk0 + nqb][:, :, (cc & ~15) | ((cc & 3) << 2) | ((cc >> 2) & 3)]
+        out["qbar"] = qbar[:, qblk0:qblk0 + nqb][:, :, (cc & ~7) | ((cc & 1) << 2) | ((cc >> 1) & 3)]
         qc = arr(lay.qcode, np.uint8, Hq * lay.q_rows * 3 * d // 4).reshape(Hq, lay.q_rows, 3 * d // 4)
         out["qcode"] = unpack(qc[:, qrow0:qrow0 + lq])
         out["qcode_pad"] = unpack(qc[:, qrow0 + lq:qrow0 + nqb * 128])
