@@ -598,8 +598,20 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
       const int idx = tid + 256 * k, key = idx / RW, ch = idx % RW;
       float f[8];
       widen8<IN>(v[k], f);
+      const v4f m0 = *reinterpret_cast<const v4f*>(kbar + 8 * ch);
+      const v4f m1 = *reinterpret_cast<const v4f*>(kbar + 8 * ch + 4);
+      const float m[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+      // the chunk's 8 channels are one MFMA-order group: channel 8 ch + e at 8 ch + mma_pos(e),
+      // the even channels first, then the odd ones
+      v4f even, odd;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kt[key * KS + mma_pos(8 * ch + e)] = key < n ? f[e] - kbar[8 * ch + e] : 0.0f;
+      for (int u = 0; u < 4; ++u) {
+        even[u] = key < n ? f[2 * u] - m[2 * u] : 0.0f;
+        odd[u] = key < n ? f[2 * u + 1] - m[2 * u + 1] : 0.0f;
+      }
+      static_assert(mma_pos(2) == 1 && mma_pos(1) == 4, "staging order must match mma_pos");
+      *reinterpret_cast<v4f*>(kt + key * KS + 8 * ch) = even;
+      *reinterpret_cast<v4f*>(kt + key * KS + 8 * ch + 4) = odd;
     }
   }
   __syncthreads();
