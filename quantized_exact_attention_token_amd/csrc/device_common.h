@@ -20,7 +20,15 @@ struct Seq {
   int32_t q_start, q_len, kv_start, kv_len, q_row0, kv_row0, qblk0, delta0;
 };
 
+// Sequence b's extents and workspace offsets. Without cu_seqlens every sequence has the full
+// lengths and the offsets follow from b (the same values the plan kernel writes, with no memory
+// read ahead of a workgroup's first loads); with them, the plan kernel's table.
 __device__ inline Seq load_seq(const KArgs& a, int b) {
+  if (!a.varlen) {
+    const int nqb = (a.Nq + kQBlock - 1) / kQBlock;
+    const int kvpad = (a.Nkv + kKVPad - 1) / kKVPad * kKVPad;
+    return Seq{0, a.Nq, 0, a.Nkv, b * nqb * kQBlock, b * kvpad, b * nqb, b * nqb * kvpad};
+  }
   const int32_t* t = reinterpret_cast<const int32_t*>(a.ws + a.lay.seq_table) + b * kSeqCols;
   Seq s;
   s.q_start = t[kQStart]; s.q_len = t[kQLen]; s.kv_start = t[kKVStart]; s.kv_len = t[kKVLen];

@@ -11,7 +11,7 @@
 // in token order over 128-token chunks, then chunks in order; f32 products and divisions, round to
 // nearest even), so its result is reproducible bit for bit. Built with -ffp-contract=off.
 //
-// The pre-pass streams Q, K and V (HBM-bound); the correction table is a small fp64 product.
+// The pre-pass streams Q, K and V (HBM-bound); the correction table is an f32 MFMA product.
 #include "device_common.h"
 
 namespace sage2 {
