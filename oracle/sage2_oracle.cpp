@@ -24,6 +24,9 @@
 // Precision: floating point that only feeds a real-valued result is carried in fp64. Floating point
 // that decides an integer (an INT4 code, an FP8 code) is evaluated in the precision the GPU kernel
 // uses (f32, IEEE round-to-nearest-even, no contraction) so that both sides take the same decision.
+// The correction term enters the logits that decide the FP8 codes, so it is an f32 chain too.
+// Parity unpinned against the pages: they print no numbers, so every pin is an invariant, a closed
+// form, a library routine or a brute-force case (tests/test_oracle_pins.py).
 // Build with -ffp-contract=off.
 
 #include <algorithm>
