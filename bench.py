@@ -93,40 +93,59 @@ def gfx_clock_under_load(launch, settle_s: float = 1.0, limit_s: float = 20.0):
 
 
 def cpu_baseline(run, w, budget_s: float = 20.0):
-    """The oracle (as it stands) on a bounded sample of the workload: kv head 0 and its q heads,
-    the full pre-pass for them, then the attention rows of an evenly spaced sample."""
+    """The oracle (as it stands) on a bounded sample of the workload: kv-head groups in order (kv
+    head g and its q heads), each with its full pre-pass and then the attention rows of an evenly
+    spaced sample, for as many groups as fit in about `budget_s` seconds (at least one)."""
     import numpy as np
     import oracle as O
+    import gpu_harness as H
 
     threads = min(os.cpu_count() or 1, 16)
-    q, k, v = run.seq_inputs(0, (0, 1))
-    t0 = time.perf_counter()
-    z = O.quantize(q, k, v, nthreads=threads)
-    t_q = time.perf_counter() - t0
-    lq, lk = q.shape[1], k.shape[1]
-    # size the row sample from a short probe so the whole baseline stays near the budget
-    probe = np.linspace(lq // 2, lq - 1, 8).astype(np.int32)
-    t0 = time.perf_counter()
-    O.attn_quant(z, w.causal, rows=probe, nthreads=threads)
-    t_probe = (time.perf_counter() - t0) / len(probe)
-    nrows = int(max(16, min(lq, (budget_s - t_q) / max(t_probe, 1e-6))))
-    rows = np.linspace(0, lq - 1, nrows).astype(np.int32)
-    t0 = time.perf_counter()
-    ref, allow = O.attn_quant(z, w.causal, rows=rows, nthreads=threads)
-    t_a = time.perf_counter() - t0
-    visible = np.minimum(rows + (lk - lq), lk - 1) + 1 if w.causal else np.full(len(rows), lk)
-    ops = 4.0 * q.shape[0] * float(np.sum(np.maximum(visible, 0))) * w.d
-    tops = ops / (t_q + t_a) / 1e12
-    # the same rows from the GPU run, for the error against the oracle
-    import gpu_harness as H
-    gpu = run.out_seq(0)[: q.shape[0], rows]
-    e = np.abs(gpu - ref)
-    # the parity tests' bar: 1e-2 + the allowance for FP8 roundings of P~ within the kernel's
-    # arithmetic error of a boundary + half an ulp of the output format
-    tol = H.MAX_ABS_TOL + allow + H.half_ulp(ref, w.dtype)
+    grp = w.Hq // w.Hkv
+    out = run.out_seq(0)
+    t_tot = ops_tot = 0.0
+    errs, gpus, refs = [], [], []
+    ng = 0
+    nrows = 0
+    t_group = 0.0
+    while ng < w.Hkv and (ng == 0 or t_tot + t_group <= budget_s):
+        q, k, v = run.seq_inputs(0, (ng, 1))
+        t0 = time.perf_counter()
+        z = O.quantize(q, k, v, nthreads=threads)
+        t_q = time.perf_counter() - t0
+        lq, lk = q.shape[1], k.shape[1]
+        if ng == 0:
+            # size the row sample from a short probe so the first group stays within the budget
+            probe = np.linspace(lq // 2, lq - 1, 8).astype(np.int32)
+            t0 = time.perf_counter()
+            O.attn_quant(z, w.causal, rows=probe, nthreads=threads)
+            t_probe = (time.perf_counter() - t0) / len(probe)
+            nrows = int(max(16, min(lq, (budget_s - t_q) / max(t_probe, 1e-6))))
+            rows = np.linspace(0, lq - 1, nrows).astype(np.int32)
+            q0, k0, v0 = q, k, v
+        t0 = time.perf_counter()
+        ref, allow = O.attn_quant(z, w.causal, rows=rows, nthreads=threads)
+        t_a = time.perf_counter() - t0
+        visible = np.minimum(rows + (lk - lq), lk - 1) + 1 if w.causal else np.full(len(rows), lk)
+        ops_tot += 4.0 * q.shape[0] * float(np.sum(np.maximum(visible, 0))) * w.d
+        t_group = t_q + t_a
+        t_tot += t_group
+        # the same rows from the GPU run, for the error against the oracle; the parity tests' bar:
+        # 1e-2 + the allowance for FP8 roundings of P~ within the kernel's arithmetic error of a
+        # boundary + half an ulp of the output format
+        gpu = out[ng * grp:(ng + 1) * grp, rows]
+        errs.append((np.abs(gpu - ref), H.MAX_ABS_TOL + allow + H.half_ulp(ref, w.dtype)))
+        gpus.append(gpu)
+        refs.append(ref)
+        ng += 1
+    tops = ops_tot / t_tot / 1e12
+    e = np.concatenate([a.ravel() for a, _ in errs])
+    tol = np.concatenate([b.ravel() for _, b in errs])
     err = {"max_abs": float(e.max()), "max_abs_beyond_tolerance": float(max(0.0, (e - tol).max())),
-           "within_tolerance": bool((e <= tol).all()), "cos": H.cos(gpu, ref),
-           "rows": int(nrows), "heads": int(q.shape[0])}
+           "within_tolerance": bool((e <= tol).all()),
+           "cos": H.cos(np.concatenate([g.ravel() for g in gpus]), np.concatenate([r.ravel() for r in refs])),
+           "rows": int(nrows), "heads": int(ng * grp)}
+    q, k, v = q0, k0, v0
     # the oracle's plain FP64 attention on a slice of the same rows (about 2 s of work)
     t0 = time.perf_counter()
     O.attn_fp64(q, k, v, w.causal, rows=probe, nthreads=threads)
@@ -147,9 +166,9 @@ def cpu_baseline(run, w, budget_s: float = 20.0):
     O.attn_quant(O.quantize(tq, tk, tv, nthreads=1), tw.causal, nthreads=1)
     t_tiny = time.perf_counter() - t0
     return ({"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
-             "sample": f"kv head 0 with its {q.shape[0]} q heads: full pre-pass, then attention "
-                       f"for {nrows} evenly spaced query rows; ops counted for those rows only, "
-                       f"time = pre-pass + rows ({t_q:.1f}s + {t_a:.1f}s)",
+             "sample": f"kv heads 0..{ng - 1} with their {ng * grp} q heads: the full pre-pass of "
+                       f"each group, then attention for {nrows} evenly spaced query rows per head; "
+                       f"ops counted for those rows only, time = pre-pass + rows ({t_tot:.1f}s)",
              "fp64_exact_value": ops64 / t_64 / 1e12,
              "fp64_exact_sample": f"the oracle's plain FP64 softmax(QK^T)V on {n64} of those rows "
                                   f"({t_64:.1f}s)",
