@@ -9,9 +9,7 @@
 
 namespace sage2 {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -39,19 +37,6 @@ __device__ inline Seq load_seq(const KArgs& a, int b) {
 template <typename T>
 __device__ inline T* ws_ptr(const KArgs& a, int64_t off) {
   return reinterpret_cast<T*>(a.ws + off);
-}
-
-// Exact widening of one fp16 / bf16 element (IN = sage2_dtype).
-template <int IN>
-__device__ inline float ld_in(const void* base, int64_t idx) {
-  const uint16_t raw = reinterpret_cast<const uint16_t*>(base)[idx];
-  if constexpr (IN == SAGE2_BF16) {
-    return __uint_as_float((uint32_t)raw << 16);
-  } else {
-    _Float16 h;
-    __builtin_memcpy(&h, &raw, 2);
-    return (float)h;
-  }
 }
 
 // Element index of (token, head, channel 0) of sequence b in a strided input.

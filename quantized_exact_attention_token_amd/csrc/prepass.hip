@@ -230,8 +230,6 @@ __device__ inline float int4_codef(float x, float inv) {
   return __builtin_amdgcn_fmed3f(rintf(x * inv), -7.0f, 7.0f) + 0.0f;
 }
 
-typedef float v16f_t __attribute__((ext_vector_type(16)));
-
 // 32 INT4 codes of consecutive channels (exact integers in float) -> 6 dwords of e2m3 (FP6) fields,
 // field i (channel i) at bits [6i, 6i + 6), little-endian across the dwords: the fp6 MFMA operand
 // format. Every integer in [-7, 7] is exact in e2m3, so the conversion is exact; the attention
@@ -239,7 +237,7 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 // exact. v_cvt_scalef32_2xpk16_fp6_f32 (scale 1) takes field 2i from element i of its first source
 // and field 2i + 1 from element i of its second (checked bit for bit against a software packing).
 __device__ inline void store_fp6_32(uint8_t* dst, const float (&c)[32]) {
-  v16f_t ev, od;
+  v16f ev, od;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     ev[i] = c[2 * i];
