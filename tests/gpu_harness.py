@@ -19,9 +19,10 @@ class GpuRun:
     """Inputs on the device, params, workspace, output."""
 
     def __init__(self, w: W.Workload, out_dtype=None, layout: str = "bnhd", device="cuda",
-                 flags: int = 0):
+                 flags: int = 0, sm_scale: float = 0.0):
         self.w = w
         self.flags = flags
+        self.sm_scale = sm_scale  # 0: the library default 1/sqrt(d)
         q, k, v, cu = W.generate(w)
         self.q_cpu, self.k_cpu, self.v_cpu, self.cu_cpu = q, k, v, cu
         dev = torch.device(device)
@@ -31,7 +32,7 @@ class GpuRun:
         odt = out_dtype or w.dtype
         self.o = torch.full(self.q.shape, float("nan"), dtype=odt, device=dev)
         self.cu = None if cu is None else cu.to(dev)
-        self.p = sage2.make_params(self.q, self.k, self.v, self.o, w.causal,
+        self.p = sage2.make_params(self.q, self.k, self.v, self.o, w.causal, sm_scale=sm_scale,
                                    cu_seqlens_q=self.cu, cu_seqlens_kv=self.cu,
                                    max_seqlen_q=w.Nq if cu is not None else None,
                                    max_seqlen_kv=w.Nkv if cu is not None else None,

@@ -37,7 +37,7 @@ def check_sequence(run: H.GpuRun, b: int, heads=None, rows=None, ws=None, check_
         # no keys: every row is fully masked and outputs zeros
         assert np.all(run.out_seq(b)[h0:h0 + nh] == 0)
         return info
-    z = O.quantize(q, k, v, flags=run.flags, nthreads=nthreads)
+    z = O.quantize(q, k, v, sm_scale=run.sm_scale, flags=run.flags, nthreads=nthreads)
     qs, kvs = slice(h0, h0 + nh), slice(g0, g0 + ng)
     _eq("kbar", dec["kbar"][kvs], z.kbar)
     _eq("sv", dec["sv"][kvs], z.sv)
@@ -72,7 +72,7 @@ def check_sequence(run: H.GpuRun, b: int, heads=None, rows=None, ws=None, check_
     ref, allow = O.attn_quant(z, w.causal, rows=rows, nthreads=nthreads)
     gpu = run.out_seq(b)[qs][:, rows]
     info.update(H.check_output(gpu, ref, allow, run.o.dtype, f"{w.name} seq {b}"))
-    exact = O.attn_fp64(q, k, v, w.causal, rows=rows, nthreads=nthreads)
+    exact = O.attn_fp64(q, k, v, w.causal, sm_scale=run.sm_scale, rows=rows, nthreads=nthreads)
     info["cos_fp64_gpu"] = H.cos(gpu, exact)
     info["cos_fp64_oracle"] = H.cos(ref, exact)
     return info

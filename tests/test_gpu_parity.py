@@ -22,8 +22,8 @@ def _report(name, info):
                                          for k, v in info.items()), flush=True)
 
 
-def _full_check(w, out_dtype=None, layout="bnhd", flags=0):
-    run = H.GpuRun(w, out_dtype=out_dtype, layout=layout, flags=flags)
+def _full_check(w, out_dtype=None, layout="bnhd", flags=0, sm_scale=0.0):
+    run = H.GpuRun(w, out_dtype=out_dtype, layout=layout, flags=flags, sm_scale=sm_scale)
     run.run()
     ws = run.ws_host()
     for b, _ in enumerate(run.sequences()):
@@ -67,6 +67,15 @@ EDGE = [
 def test_edge_shapes(case):
     B, Hq, Hkv, Nq, Nkv, d, dt, causal = case
     _full_check(W.custom(B, Hq, Hkv, Nq, Nkv, d, dt, causal, seed=Nq * 7 + Nkv))
+
+
+@pytest.mark.parametrize("case", [(0.05, 128, torch.bfloat16, True), (0.3, 64, torch.float16, False),
+                                  (0.125, 96, torch.bfloat16, True)],
+                         ids=["tau0.05_d128_causal", "tau0.3_d64_full", "tau0.125_d96_causal"])
+def test_custom_softmax_scale(case):
+    """A caller-given softmax scale (not 1/sqrt(d)) reaches the correction table and the logits."""
+    tau, d, dt, causal = case
+    _full_check(W.custom(1, 4, 2, 300, 300, d, dt, causal, seed=int(tau * 1000) + d), sm_scale=tau)
 
 
 def test_bhnd_strides():
