@@ -42,7 +42,8 @@ class Workload:
     k_offset_rademacher: float = 0.0  # K += a * (+-1) per (kv head, channel)
     n_outliers: int = 0
     outlier_scale: float = 1.0
-    seqlens: list | None = None     # packed variable-length batch: per-sequence lengths (Nq == Nkv)
+    seqlens: list | None = None     # packed variable-length batch: per-sequence (query) lengths
+    kv_seqlens: list | None = None  # per-sequence key/value lengths when they differ from seqlens
     key_ramp: float = 0.0           # K[j] += key_ramp * j / Nkv (all channels)
     q_shift: float = 0.0            # Q += q_shift (all channels)
     extra: dict = field(default_factory=dict)
@@ -51,23 +52,35 @@ class Workload:
     def varlen(self) -> bool:
         return self.seqlens is not None
 
+    @property
+    def kv_lens(self) -> list | None:
+        return self.kv_seqlens if self.kv_seqlens is not None else self.seqlens
+
     def attention_ops(self) -> float:
         """4 * Nq * Nkv * d per (sequence, q head): one INT4 MAC and one FP8 MAC per (q, k, channel),
         two ops each; halved under a causal mask."""
         if self.varlen:
-            tot = sum(4.0 * self.Hq * L * L * self.d for L in self.seqlens)
+            tot = sum(4.0 * self.Hq * lq * lk * self.d for lq, lk in zip(self.seqlens, self.kv_lens))
         else:
             tot = 4.0 * self.B * self.Hq * self.Nq * self.Nkv * self.d
         return tot / 2 if self.causal else tot
 
 
+def cu_seqlens(lens) -> torch.Tensor:
+    """Offsets int32 [len(lens) + 1] of a packed batch with these per-sequence lengths."""
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int32), 0)
+    return cu
+
+
 def generate(w: Workload):
     """Returns (q, k, v, cu_seqlens) on the CPU. Dense: q [B, Nq, Hq, d], k/v [B, Nkv, Hkv, d].
-    Variable length: q/k/v packed [total, H, d] and cu_seqlens int32 [nseq + 1]."""
+    Variable length: q/k/v packed [total, H, d] and the query offsets cu_seqlens int32 [nseq + 1]
+    (the key/value offsets are cu_seqlens(w.kv_lens))."""
     g = torch.Generator().manual_seed(w.seed)
     B = 1 if w.varlen else w.B
     Nq = sum(w.seqlens) if w.varlen else w.Nq
-    Nkv = sum(w.seqlens) if w.varlen else w.Nkv
+    Nkv = sum(w.kv_lens) if w.varlen else w.Nkv
     q = torch.randn(B, Nq, w.Hq, w.d, generator=g, dtype=torch.float32)
     k = torch.randn(B, Nkv, w.Hkv, w.d, generator=g, dtype=torch.float32)
     v = torch.randn(B, Nkv, w.Hkv, w.d, generator=g, dtype=torch.float32)
@@ -90,9 +103,7 @@ def generate(w: Workload):
         q += w.q_shift
     q, k, v = q.to(w.dtype), k.to(w.dtype), v.to(w.dtype)
     if w.varlen:
-        cu = torch.zeros(len(w.seqlens) + 1, dtype=torch.int32)
-        cu[1:] = torch.cumsum(torch.tensor(w.seqlens, dtype=torch.int32), 0)
-        return q[0].contiguous(), k[0].contiguous(), v[0].contiguous(), cu
+        return q[0].contiguous(), k[0].contiguous(), v[0].contiguous(), cu_seqlens(w.seqlens)
     return q, k, v, None
 
 
@@ -126,9 +137,9 @@ SWEEP = {
 
 
 def custom(B, Hq, Hkv, Nq, Nkv, d, dtype=torch.bfloat16, causal=False, seed=0, seqlens=None,
-           **kw) -> Workload:
+           kv_seqlens=None, **kw) -> Workload:
     """Small cases for edge tests: same recipe family as the tiny workload unless overridden."""
     base = dict(k_offset_std=3.0, n_outliers=min(2, d), outlier_scale=10.0)
     base.update(kw)
     return Workload(f"custom_s{seed}", B, Hq, Hkv, Nq, Nkv, d, dtype, causal, seed,
-                    seqlens=seqlens, **base)
+                    seqlens=seqlens, kv_seqlens=kv_seqlens, **base)

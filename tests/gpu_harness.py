@@ -25,6 +25,7 @@ class GpuRun:
         self.sm_scale = sm_scale  # 0: the library default 1/sqrt(d)
         q, k, v, cu = W.generate(w)
         self.q_cpu, self.k_cpu, self.v_cpu, self.cu_cpu = q, k, v, cu
+        self.cu_kv_cpu = None if cu is None else W.cu_seqlens(w.kv_lens)
         dev = torch.device(device)
         if layout == "bhnd" and cu is None:  # same values, [B, H, N, d] storage seen through strides
             q, k, v = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
@@ -32,8 +33,9 @@ class GpuRun:
         odt = out_dtype or w.dtype
         self.o = torch.full(self.q.shape, float("nan"), dtype=odt, device=dev)
         self.cu = None if cu is None else cu.to(dev)
+        self.cu_kv = None if cu is None else self.cu_kv_cpu.to(dev)
         self.p = sage2.make_params(self.q, self.k, self.v, self.o, w.causal, sm_scale=sm_scale,
-                                   cu_seqlens_q=self.cu, cu_seqlens_kv=self.cu,
+                                   cu_seqlens_q=self.cu, cu_seqlens_kv=self.cu_kv,
                                    max_seqlen_q=w.Nq if cu is not None else None,
                                    max_seqlen_kv=w.Nkv if cu is not None else None,
                                    flags=flags)
@@ -69,8 +71,8 @@ class GpuRun:
         """[(q_len, kv_len)] per sequence."""
         if self.cu_cpu is None:
             return [(self.w.Nq, self.w.Nkv)] * self.w.B
-        cu = self.cu_cpu.numpy()
-        return [(int(cu[i + 1] - cu[i]),) * 2 for i in range(len(cu) - 1)]
+        cq, ck = self.cu_cpu.numpy(), self.cu_kv_cpu.numpy()
+        return [(int(cq[i + 1] - cq[i]), int(ck[i + 1] - ck[i])) for i in range(len(cq) - 1)]
 
     def decode(self, ws: np.ndarray, b: int):
         """Canonical pre-pass outputs of sequence b, shaped like the oracle's (the head dim's zero
@@ -140,7 +142,8 @@ class GpuRun:
             q, k, v = self.q_cpu[b], self.k_cpu[b], self.v_cpu[b]
         else:
             s, e = int(self.cu_cpu[b]), int(self.cu_cpu[b + 1])
-            q, k, v = self.q_cpu[s:e], self.k_cpu[s:e], self.v_cpu[s:e]
+            sk, ek = int(self.cu_kv_cpu[b]), int(self.cu_kv_cpu[b + 1])
+            q, k, v = self.q_cpu[s:e], self.k_cpu[sk:ek], self.v_cpu[sk:ek]
         if heads is not None:
             g0, ng = heads
             grp = self.w.Hq // self.w.Hkv

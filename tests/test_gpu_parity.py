@@ -88,6 +88,21 @@ def test_varlen_with_empty_sequences():
     _full_check(w)
 
 
+@pytest.mark.parametrize("case", [
+    # (d, dtype, causal, query lengths, key/value lengths)
+    (64, torch.float16, True, [100, 0, 257, 33], [300, 64, 128, 0]),
+    (128, torch.bfloat16, False, [200, 129, 5], [77, 300, 130]),
+], ids=["d64_causal", "d128_full"])
+def test_varlen_different_kv_lengths(case):
+    """Packed batches whose query and key/value lengths differ per sequence: fewer queries than keys
+    (bottom-right causal alignment), more queries than keys (leading rows see no key), empty query
+    or key sets."""
+    d, dt, causal, lq, lk = case
+    w = W.custom(len(lq), 4, 2, max(lq), max(lk), d, dt, causal, seed=sum(lq) + 3 * sum(lk),
+                 seqlens=lq, kv_seqlens=lk)
+    _full_check(w)
+
+
 def test_varlen_equals_separate_calls():
     """E1: a packed variable-length batch gives bit-identical outputs to one call per sequence."""
     lens = [100, 257, 64]
