@@ -32,6 +32,9 @@ class GpuRun:
         self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
         odt = out_dtype or w.dtype
         self.o = torch.full(self.q.shape, float("nan"), dtype=odt, device=dev)
+        if layout == "bhnd" and cu is None:  # the output in [B, H, N, d] storage as well
+            B_, N_, H_, d_ = self.q.shape
+            self.o = torch.full((B_, H_, N_, d_), float("nan"), dtype=odt, device=dev).permute(0, 2, 1, 3)
         self.cu = None if cu is None else cu.to(dev)
         self.cu_kv = None if cu is None else self.cu_kv_cpu.to(dev)
         self.p = sage2.make_params(self.q, self.k, self.v, self.o, w.causal, sm_scale=sm_scale,
