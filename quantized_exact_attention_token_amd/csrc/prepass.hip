@@ -645,7 +645,7 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
 
 // ---- the K/V quantizer and the correction table in one launch ----------------------------------
 // The two read the statistics of the previous kernels and not each other's output; run side by
-// side, the HBM-bound quantizer workgroups fill the CUs next to the fp64-MFMA-bound correction
+// side, the HBM-bound quantizer workgroups fill the CUs next to the MFMA-bound correction
 // workgroups as the correction workgroups drain. grid (2 x 64-key tiles x H_kv, 1, B): first the
 // correction workgroups, x = tile * H_kv + kv head (longest first under a causal mask), then the
 // quantizer workgroups in the same order. (Quantizers first, or the two roles interleaved, measured
