@@ -103,7 +103,10 @@ typedef struct {
 /* Byte offsets (from the workspace base) and byte sizes of the workspace buffers, for tests that
  * decode the pre-pass outputs. Row counts are padded per sequence: Q rows to a multiple of 128,
  * K/V rows to a multiple of 128. Layouts (head-major; "row" = padded token slot):
- *   seq_table  int32 [B][8]: q_start, q_len, kv_start, kv_len, q_row0, kv_row0, qblk0, delta0
+ *   seq_table  int32 [B][8]: q_start, q_len, kv_start, kv_len, q_row0, kv_row0, qblk0, delta0;
+ *                                             written for variable-length batches only (without
+ *                                             cu_seqlens sequence b has q_len N_q, kv_len N_kv,
+ *                                             starts 0 and the offsets of b full sequences)
  *   k_partial  f64   [H_kv][kv_rows/128][d]   per-128-token fp64 sums of K
  *   v_partial  f32   [H_kv][kv_rows/128][d]   per-128-token max |V|
  *   kbar       f32   [B][H_kv][d]             K channel means

@@ -18,7 +18,7 @@ namespace sage2 {
 namespace {
 
 // ---- plan: per-sequence offsets into the padded workspace buffers ------------------------------
-// One thread walks the sequences in order. A sequence whose device lengths disagree with what the
+// Launched for variable-length batches only. One thread walks the sequences in order. A sequence whose device lengths disagree with what the
 // host sized the workspace for (lengths above N, or totals past the layout) gets length 0, so no
 // kernel touches memory outside the workspace.
 __global__ void k_plan(KArgs a) {
@@ -665,7 +665,8 @@ int launch_all(const KArgs& a, hipStream_t st) {
   const int nch = (a.Nkv + kKVPad - 1) / kKVPad;
   const int nqb = (a.Nq + kQBlock - 1) / kQBlock;
   const int ntile = nch * (kKVPad / kKVTile);
-  k_plan<<<1, 64, 0, st>>>(a);
+  // without cu_seqlens the kernels compute each sequence's offsets from its index (load_seq)
+  if (a.varlen) k_plan<<<1, 64, 0, st>>>(a);
   k_stats_quant_q<D, IN><<<dim3(nch * a.Hkv + nqb * a.Hq, 1, a.B), 256, 0, st>>>(a, nch);
   k_kreduce<D><<<dim3(D / 32, a.Hkv, a.B), 256, 0, st>>>(a);
   k_kv_delta<D, IN><<<dim3(2 * ntile * a.Hkv, 1, a.B), 256, 0, st>>>(a, ntile);

@@ -83,8 +83,14 @@ class GpuRun:
         lay, w = self.lay, self.w
         dt, Hq, Hkv = w.d, w.Hq, w.Hkv
         d = 64 if dt <= 64 else 128  # head dim inside the workspace
-        tab = ws[lay.seq_table:lay.seq_table + 4 * 8 * self.p.B].view(np.int32).reshape(-1, 8)
-        qs, lq, ks, lk, qrow0, kvrow0, qblk0, delta0 = (int(x) for x in tab[b])
+        if self.cu_cpu is None:
+            # no table without cu_seqlens: sequence b sits after b full sequences
+            nqb_, kvpad_ = (w.Nq + 127) // 128, (w.Nkv + 127) // 128 * 128
+            qs, lq, ks, lk = 0, w.Nq, 0, w.Nkv
+            qrow0, kvrow0, qblk0, delta0 = b * nqb_ * 128, b * kvpad_, b * nqb_, b * nqb_ * kvpad_
+        else:
+            tab = ws[lay.seq_table:lay.seq_table + 4 * 8 * self.p.B].view(np.int32).reshape(-1, 8)
+            qs, lq, ks, lk, qrow0, kvrow0, qblk0, delta0 = (int(x) for x in tab[b])
         nqb = (lq + 127) // 128
         kvpad = (lk + 127) // 128 * 128
 
