@@ -291,7 +291,10 @@ def main():
     traffic = traffic_per_launch(w.name)
     roofline = {"bound": "mfma", "achieved": kernel_tops, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": kernel_tops / PEAK_TOPS, "traffic": traffic,
-                "kernel": "k_attn (sage2_attn_fwd)", "ops_per_launch": ops,
+                "kernel": "k_attn (sage2_attn_fwd)",
+                "limiter": "VALU issue: the online softmax's per-element arithmetic (dequantize, max, "
+                           "exp, row sum, fp8 conversion, fold), not the MFMA",
+                "ops_per_launch": ops,
                 "avg_launch_ms": att_avg}
 
     out = {
