@@ -280,9 +280,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
 
   const DmaPlan<D> plan = make_dma_plan<D>(wave, lane);
   // per-lane LDS byte offsets of the compute reads (loop invariant)
-  int kofs[4];
+  int kofs[4], kofs24[4];
 #pragma unroll
   for (int sub = 0; sub < 4; ++sub) kofs[sub] = S::K_OFF + 16 * k_block<D>(32 * sub + n, S::R / 2 * hh);
+  // the same offsets + 24, computed where the compiler cannot see the relation (see the K operand
+  // reads below)
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) asm("v_add_u32 %0, 24, %1" : "=v"(kofs24[sub]) : "v"(kofs[sub]));
   int vofs[NCB][2][2];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -310,13 +314,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
       for (int sub = 0; sub < 4; ++sub) {
         v16f acc = v16f{};
         if constexpr (D == 128) {
-          // this lane's 48 bytes of the key row (rows keep their 3-block halves contiguous). The
-          // compiler merges the two middle 8-byte reads into one 16-byte read and splits it over
-          // the two operand tuples with two register copies; keeping the reads apart removes the
-          // copies but costs a fourth LDS read per subtile, which measured slower
+          // this lane's 48 bytes of the key row (rows keep their 3-block halves contiguous), as
+          // 16 + 8 bytes per operand. Addressed from the same base, the compiler merges the two
+          // middle 8-byte reads into one 16-byte read and then splits it over the two operand
+          // tuples with register copies (14 per tile); with the second one addressed from the
+          // opaque kofs24 the reads stay apart and land in place
           const uint4 b0 = *reinterpret_cast<const uint4*>(st + kofs[sub]);
           const uint2 b1 = *reinterpret_cast<const uint2*>(st + kofs[sub] + 16);
-          const uint2 b2 = *reinterpret_cast<const uint2*>(st + kofs[sub] + 24);
+          const uint2 b2 = *reinterpret_cast<const uint2*>(st + kofs24[sub]);
           const uint4 b3 = *reinterpret_cast<const uint4*>(st + kofs[sub] + 32);
           const v8i k0 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, 0, 0};
           const v8i k1 = {(int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y, (int)b3.z, (int)b3.w, 0, 0};
