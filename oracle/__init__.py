@@ -23,7 +23,12 @@ _LIB = os.path.join(_HERE, "libsage2_oracle.so")
 NO_K_SMOOTH = 1
 NO_Q_SMOOTH = 2
 PER_BLOCK = 4
-ATTN_NO_P8 = 1
+DELTA_F64 = 8          # correction term as one fp64 dot product (alternative reading, evidence only)
+ATTN_NO_P8 = 1         # P~ unquantized
+ATTN_V_EXACT = 2       # error budget: unquantized V
+ATTN_QK_EXACT = 4      # error budget: logits from the unquantized Q, K
+ATTN_NARROW_ACC = 8    # ablation: P~V sums in a float of `acc_bits` mantissa bits
+ATTN_SINGLE_LEVEL = 16  # ablation: no FP32 fold
 
 _lib = None
 
@@ -49,7 +54,8 @@ def lib():
         L.orc_quantize.argtypes = [I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, P, P, P, P, I]
         L.orc_qk_i32.argtypes = [I, I, I, I, I, P, P, I, I, P, I]
         L.orc_logits.argtypes = [I, I, I, I, I, F, I, P, P, P, P, P, P, I, P, I]
-        L.orc_attn_quant.argtypes = [I, I, I, I, I, F, I, I, I, P, P, P, P, P, P, P, P, I, P, P, I]
+        L.orc_attn_quant.argtypes = [I, I, I, I, I, F, I, I, I, P, P, P, P, P, P, P, P, I, P, P,
+                                     P, P, P, P, P, I, P, I, I]
         L.orc_attn_fp64.argtypes = [I, I, I, I, I, F, I, P, P, P, P, I, P, I]
         L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_decode.restype = ctypes.c_double
@@ -146,18 +152,39 @@ def logits(z: Quantized, causal: bool, rows=None, nthreads: int = 0):
 
 
 def attn_quant(z: Quantized, causal: bool, rows=None, bn: int = 128, flags: int = 0,
-               nthreads: int = 0):
+               nthreads: int = 0, exact=None, codes: bool = False, acc_bits: int = 0,
+               band_log2: int = 0):
     """Returns (out, allow): [Hq, nrows, d] float64 each. `allow` bounds the effect of FP8
-    roundings of P~ that sit within the kernel's arithmetic error of a rounding boundary."""
+    roundings of P~ that sit within the kernel's arithmetic error of a rounding boundary.
+
+    exact = (q, k, v) float32 head-major unquantized inputs, for ATTN_QK_EXACT / ATTN_V_EXACT.
+    codes=True adds (p8, amb) [Hq, nrows, Lkv] uint8: each P~ code and whether it is ambiguous.
+    band_log2 > 0 adds the single-level accumulation error band [Hq, nrows, d] (relative error
+    2^-band_log2 per 64-key step). Extra outputs follow (out, allow) in that order."""
     r, n = _rows(rows, z.Lq)
     out = np.zeros((z.Hq, n, z.d), np.float64)
     allow = np.zeros((z.Hq, n, z.d), np.float64)
+    qe = ke = ve = None
+    if exact is not None:
+        qe, ke, ve = (_f32(a) for a in exact)
+    p8 = amb = band = None
+    if codes:
+        p8 = np.zeros((z.Hq, n, z.Lkv), np.uint8)
+        amb = np.zeros((z.Hq, n, z.Lkv), np.uint8)
+    if band_log2:
+        band = np.zeros((z.Hq, n, z.d), np.float64)
     rc = lib().orc_attn_quant(z.Hq, z.Hkv, z.Lq, z.Lkv, z.d, z.sm_scale, int(causal), bn, flags,
                               _p(z.qcode), _p(z.sq), _p(z.kcode), _p(z.sk), _p(z.v8), _p(z.sv),
-                              _p(z.delta), _p(r), n, _p(out), _p(allow), nthreads)
+                              _p(z.delta), _p(r), n, _p(out), _p(allow), _p(qe), _p(ke), _p(ve),
+                              _p(p8), _p(amb), int(acc_bits), _p(band), int(band_log2), nthreads)
     if rc != 0:
         raise ValueError("orc_attn_quant rejected its arguments")
-    return out, allow
+    res = (out, allow)
+    if codes:
+        res += (p8, amb)
+    if band_log2:
+        res += (band,)
+    return res
 
 
 def attn_fp64(q, k, v, causal: bool, sm_scale: float = 0.0, rows=None, nthreads: int = 0):

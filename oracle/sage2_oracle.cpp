@@ -138,9 +138,19 @@ enum {
   ORC_PER_BLOCK = 4,    // ablation: per-block scales (one per 128-token Q block, one per 64-key K
                         // block) in place of the per-thread ones ([VIZ] Per-Thread INT4 Geometry
                         // contrasts the two)
+  ORC_DELTA_F64 = 8,    // the correction term as one fp64 dot product rounded once to f32 (the other
+                        // plain reading of "exact correction"; used to show that the choice of the
+                        // f32 chain moves the output by far less than the parity bar)
 };
 enum {
-  ORC_ATTN_NO_P8 = 1,   // keep P~ unquantized (used to compare the online form with a two-pass form)
+  ORC_ATTN_NO_P8 = 1,       // keep P~ unquantized (online form vs two-pass form; error budget)
+  ORC_ATTN_V_EXACT = 2,     // error budget: the unquantized V in place of s_v * dec(v8)
+  ORC_ATTN_QK_EXACT = 4,    // error budget: logits from the unquantized Q, K (L * q.k in fp64,
+                            // rounded to f32) in place of the INT4 path
+  ORC_ATTN_NARROW_ACC = 8,  // ablation: the P~V sums are held in a float of `acc_bits` mantissa bits
+                            // (round to nearest even after every 32 keys and after each rescale)
+  ORC_ATTN_SINGLE_LEVEL = 16, // ablation: no FP32 fold; the running output itself is the
+                            // accumulator that each tile's products are added to
 };
 
 double orc_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
@@ -272,6 +282,13 @@ int orc_quantize(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int fl
       if (delta) {
         float* D = delta + ((size_t)h * nqb + b) * Lkv;
         for (int j = 0; j < Lkv; ++j) {
+          if (flags & ORC_DELTA_F64) {
+            // alternative reading: one fp64 dot product, scaled in fp64, rounded once to f32
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += (double)qb[c] * (double)KT[(size_t)j * d + c];
+            D[j] = (float)(acc * (double)L);
+            continue;
+          }
           float acc = 0.0f;
           for (int c = 0; c < d; ++c) acc = std::fmaf(qb[c], KT[(size_t)j * d + c], acc);
           D[j] = acc * L;
@@ -367,74 +384,165 @@ int orc_logits(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int caus
 // `allow` bounds how far such flips can move it:
 // allow = (sum over ambiguous j of |code step| * |dec(v8[j,c])| * rescale) * s_v[c] / l.
 //
-// q-side inputs are the orc_quantize outputs of the same sequence. out/allow: [Hq][nrows][d] f64.
+// Optional outputs and modes (all off by default):
+//   p8_out / amb_out [Hq][nrows][Lkv] u8: the P~ code of every (row, key) and 1 where it is
+//     ambiguous (masked keys, and keys of tiles before the row's first visible key, give code 0);
+//   ORC_ATTN_V_EXACT / ORC_ATTN_QK_EXACT: q_exact [Hq][Lq][d], k_exact / v_exact [Hkv][Lkv][d] f32
+//     replace the quantized operands, for an error budget of each quantizer on its own;
+//   ORC_ATTN_NARROW_ACC (acc_bits) and ORC_ATTN_SINGLE_LEVEL: accumulation ablations. The narrow
+//     accumulator keeps acc_bits mantissa bits (unbounded exponent) and rounds to nearest even after
+//     each 32-key group's exact sum is added and after each rescale; with the two-level form only
+//     the per-tile inner sum is narrow and the fold into O is exact, with the single-level form O
+//     itself is the accumulator. `band` (optional, [Hq][nrows][d]) returns, for the single-level
+//     form with exact accumulation, the bound sum over 64-key steps of
+//     2^-band_log2 * (|O after the step| + sum_j |P~_j| |v_j|) * s_v / l (rescaled like O): the
+//     error that an accumulator adding each 64-key step with a relative error of at most
+//     2^-band_log2 of those magnitudes could reach.
+namespace {
+
+// round to nearest even at `bits` mantissa bits after the leading one (unbounded exponent)
+double round_bits(double x, int bits) {
+  if (x == 0.0 || !std::isfinite(x)) return x;
+  const int e = std::ilogb(x);
+  const double q = std::ldexp(1.0, e - bits);
+  return std::nearbyint(x / q) * q;
+}
+
+}  // namespace
+
 int orc_attn_quant(int Hq, int Hkv, int Lq, int Lkv, int d, float sm_scale, int causal, int bn,
                    int flags, const int8_t* qcode, const float* sq, const int8_t* kcode,
                    const float* sk, const uint8_t* v8, const float* sv, const float* delta,
-                   const int32_t* rows, int nrows, double* out, double* allow, int nthreads) {
+                   const int32_t* rows, int nrows, double* out, double* allow,
+                   const float* q_exact, const float* k_exact, const float* v_exact,
+                   uint8_t* p8_out, uint8_t* amb_out, int acc_bits, double* band, int band_log2,
+                   int nthreads) {
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lq <= 0 || Lkv <= 0 || bn <= 0) return -1;
+  if ((flags & ORC_ATTN_V_EXACT) && !v_exact) return -1;
+  if ((flags & ORC_ATTN_QK_EXACT) && (!q_exact || !k_exact)) return -1;
+  if ((flags & ORC_ATTN_NARROW_ACC) && (acc_bits < 1 || acc_bits > 52)) return -1;
   if (!rows) nrows = Lq;
-  LogitCtx ctx{Hq, Hkv, Lq, Lkv, d, causal, resolve_scale(sm_scale, d) * kLog2e,
-               qcode, kcode, sq, sk, delta, 2 * ceil_div(Lkv, 32), ceil_div(Lq, kQBlock)};
+  const float L = resolve_scale(sm_scale, d) * kLog2e;
+  LogitCtx ctx{Hq, Hkv, Lq, Lkv, d, causal, L, qcode, kcode, sq, sk, delta, 2 * ceil_div(Lkv, 32),
+               ceil_div(Lq, kQBlock)};
   double vdec[256];
   for (int c = 0; c < 256; ++c) vdec[c] = e4m3_decode((uint8_t)c);
+  const bool narrow = flags & ORC_ATTN_NARROW_ACC, single = flags & ORC_ATTN_SINGLE_LEVEL;
+  const double band_eps = std::ldexp(1.0, -band_log2);
   parallel_for(Hq * nrows, resolve_threads(nthreads), [&](int unit) {
     const int h = unit / nrows, r = unit % nrows;
     const int i = rows ? rows[r] : r;
     const int g = h / (Hq / Hkv);
-    std::vector<double> O(d, 0.0), A(d, 0.0), inner(d), ainner(d);
+    std::vector<double> O(d, 0.0), A(d, 0.0), B(d, 0.0), inner(d), ainner(d), vrow(d), chunk(d),
+        absprod(d);
     std::vector<float> x(bn);
+    uint8_t* p8r = p8_out ? p8_out + ((size_t)h * nrows + r) * Lkv : nullptr;
+    uint8_t* ambr = amb_out ? amb_out + ((size_t)h * nrows + r) * Lkv : nullptr;
+    if (p8r) std::fill(p8r, p8r + Lkv, 0);
+    if (ambr) std::fill(ambr, ambr + Lkv, 0);
     float m = -kInfF;
     double l = 0.0;
     for (int t0 = 0; t0 < Lkv; t0 += bn) {
       const int t1 = std::min(Lkv, t0 + bn);
       float tmax = -kInfF;
       for (int j = t0; j < t1; ++j) {
-        x[j - t0] = logit(ctx, h, i, j);
-        tmax = std::max(tmax, x[j - t0]);
+        float xj;
+        if (flags & ORC_ATTN_QK_EXACT) {
+          if (causal && j > i + (Lkv - Lq)) {
+            xj = -kInfF;
+          } else {
+            const float* qi = q_exact + ((size_t)h * Lq + i) * d;
+            const float* kj = k_exact + ((size_t)g * Lkv + j) * d;
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += (double)qi[c] * (double)kj[c];
+            xj = (float)((double)L * acc);
+          }
+        } else {
+          xj = logit(ctx, h, i, j);
+        }
+        x[j - t0] = xj;
+        tmax = std::max(tmax, xj);
       }
       const float mnew = std::max(m, tmax);
       if (mnew == -kInfF) continue;  // no visible key yet: nothing to add, nothing to rescale
       const double alpha = (m == -kInfF) ? 0.0 : std::exp2((double)m - (double)mnew);
       const float mb = mnew - kLog2_448;
-      std::fill(inner.begin(), inner.end(), 0.0);
+      // single-level: the running output is rescaled in place (in the accumulator's format)
+      if (single) {
+        for (int c = 0; c < d; ++c) {
+          O[c] = narrow ? round_bits(alpha * O[c], acc_bits) : alpha * O[c];
+          A[c] *= alpha;
+          B[c] *= alpha;
+        }
+      }
+      std::vector<double>& acc = single ? O : inner;
+      if (!single) std::fill(inner.begin(), inner.end(), 0.0);
       std::fill(ainner.begin(), ainner.end(), 0.0);
+      std::fill(chunk.begin(), chunk.end(), 0.0);
+      std::fill(absprod.begin(), absprod.end(), 0.0);
       double psum = 0.0;
       for (int j = t0; j < t1; ++j) {
         const float xj = x[j - t0];
-        if (xj == -kInfF) continue;
-        const float t = xj - mb;
-        const double p = std::exp2((double)t);
-        psum += p;
-        double p8 = p, step = 0.0;
-        if (!(flags & ORC_ATTN_NO_P8)) {
-          const uint8_t code = e4m3_encode(p);
-          p8 = e4m3_decode(code);
-          const double rad = 0x1p-22;
-          const uint8_t lo = e4m3_encode(std::exp2((double)t - rad));
-          const uint8_t hi = e4m3_encode(std::exp2((double)t + rad));
-          if (lo != hi)
-            step = std::max(std::fabs(e4m3_decode(lo) - p8), std::fabs(e4m3_decode(hi) - p8));
+        if (xj != -kInfF) {
+          const float t = xj - mb;
+          const double p = std::exp2((double)t);
+          psum += p;
+          double p8 = p, step = 0.0;
+          if (!(flags & ORC_ATTN_NO_P8)) {
+            const uint8_t code = e4m3_encode(p);
+            p8 = e4m3_decode(code);
+            const double rad = 0x1p-22;
+            const uint8_t lo = e4m3_encode(std::exp2((double)t - rad));
+            const uint8_t hi = e4m3_encode(std::exp2((double)t + rad));
+            if (lo != hi)
+              step = std::max(std::fabs(e4m3_decode(lo) - p8), std::fabs(e4m3_decode(hi) - p8));
+            if (p8r) p8r[j] = code;
+            if (ambr) ambr[j] = lo != hi;
+          }
+          if (flags & ORC_ATTN_V_EXACT) {
+            const float* ve = v_exact + ((size_t)g * Lkv + j) * d;
+            for (int c = 0; c < d; ++c) vrow[c] = ve[c];
+          } else {
+            const uint8_t* vr = v8 + ((size_t)g * Lkv + j) * d;
+            for (int c = 0; c < d; ++c) vrow[c] = vdec[vr[c]];
+          }
+          for (int c = 0; c < d; ++c) {
+            chunk[c] += p8 * vrow[c];
+            absprod[c] += std::fabs(p8 * vrow[c]);
+            if (step != 0.0) ainner[c] += step * std::fabs(vrow[c]);
+          }
         }
-        const uint8_t* vrow = v8 + ((size_t)g * Lkv + j) * d;
-        for (int c = 0; c < d; ++c) {
-          inner[c] += p8 * vdec[vrow[c]];
-          if (step != 0.0) ainner[c] += step * std::fabs(vdec[vrow[c]]);
+        // the exact sum of each 32-key group is added to the accumulator (one rounding when narrow)
+        if ((j - t0) % 32 == 31 || j == t1 - 1) {
+          for (int c = 0; c < d; ++c) {
+            acc[c] = narrow ? round_bits(acc[c] + chunk[c], acc_bits) : acc[c] + chunk[c];
+            chunk[c] = 0.0;
+          }
+        }
+        // error band of the single-level form: one term per 64-key step
+        if (band && ((j - t0) % 64 == 63 || j == t1 - 1)) {
+          for (int c = 0; c < d; ++c) {
+            B[c] += band_eps * (std::fabs(acc[c]) + absprod[c]);
+            absprod[c] = 0.0;
+          }
         }
       }
       l = alpha * l + psum;
       for (int c = 0; c < d; ++c) {
-        O[c] = alpha * O[c] + inner[c];
-        A[c] = alpha * A[c] + ainner[c];
+        if (!single) O[c] = alpha * O[c] + inner[c];
+        if (!single) A[c] = alpha * A[c] + ainner[c];
+        else A[c] += ainner[c];
       }
       m = mnew;
     }
     double* o = out + ((size_t)h * nrows + r) * d;
     double* a = allow ? allow + ((size_t)h * nrows + r) * d : nullptr;
+    double* bb = band ? band + ((size_t)h * nrows + r) * d : nullptr;
     for (int c = 0; c < d; ++c) {
-      const double s = sv[(size_t)g * d + c];
+      const double s = (flags & ORC_ATTN_V_EXACT) ? 1.0 : sv[(size_t)g * d + c];
       o[c] = l > 0.0 ? O[c] * s / l : 0.0;
       if (a) a[c] = l > 0.0 ? A[c] * s / l : 0.0;
+      if (bb) bb[c] = l > 0.0 ? B[c] * s / l : 0.0;
     }
   });
   return 0;
