@@ -23,7 +23,7 @@ _LIB = os.path.join(_HERE, "libsage2_oracle.so")
 NO_K_SMOOTH = 1
 NO_Q_SMOOTH = 2
 PER_BLOCK = 4
-DELTA_F64 = 8          # correction term as one fp64 dot product (alternative reading, evidence only)
+DELTA_F64 = 16         # correction term as one fp64 dot product (alternative reading, evidence only)
 ATTN_NO_P8 = 1         # P~ unquantized
 ATTN_V_EXACT = 2       # error budget: unquantized V
 ATTN_QK_EXACT = 4      # error budget: logits from the unquantized Q, K

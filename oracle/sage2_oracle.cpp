@@ -138,7 +138,7 @@ enum {
   ORC_PER_BLOCK = 4,    // ablation: per-block scales (one per 128-token Q block, one per 64-key K
                         // block) in place of the per-thread ones ([VIZ] Per-Thread INT4 Geometry
                         // contrasts the two)
-  ORC_DELTA_F64 = 8,    // the correction term as one fp64 dot product rounded once to f32 (the other
+  ORC_DELTA_F64 = 16,   // the correction term as one fp64 dot product rounded once to f32 (the other
                         // plain reading of "exact correction"; used to show that the choice of the
                         // f32 chain moves the output by far less than the parity bar)
 };
