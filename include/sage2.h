@@ -160,11 +160,20 @@ const char* sage2_status_string(sage2_status s);
 /* Workspace layout of p (host struct). */
 sage2_status sage2_workspace_layout(const sage2_params* p, sage2_ws_layout* out);
 
-/* Exact INT32 Q K^T of the INT4 codes, computed by the attention kernel's own MFMA path, for query
- * rows [q_begin, q_begin + q_count) of every sequence and q head: s_out (device) int32
- * [B][H_q][q_count][N_kv]; entries past a sequence's lengths are written as 0. */
-sage2_status sage2_debug_qk_i32(const sage2_params* p, const void* ws, size_t ws_bytes,
-                                int32_t q_begin, int32_t q_count, int32_t* s_out, void* stream);
+/* The attention kernel itself (sage2_attn_fwd's kernel, two-level form), additionally writing for
+ * query rows [q_begin, q_begin + q_count) of every sequence and q head what its tiles compute:
+ *   s_out  (device, may be NULL) int32 [B][H_q][q_count][N_kv]: the exact INT32 Q K^T of the INT4
+ *          codes, taken from the same LDS-staged operands and MFMAs that feed the softmax (abstract:
+ *          INT4 Q K^T; visual companion, "Numerical Repair Stack": exact INT4 fragments);
+ *   p8_out (device, may be NULL) uint8 [B][H_q][q_count][N_kv]: the e4m3 code of P~ that the kernel
+ *          feeds to its P~V MFMA for each key (abstract: P~ to FP8); 0 for masked keys.
+ * Only the key tiles a row's wave visits are written (under a causal mask, tiles past the wave's last
+ * visible key are skipped); other entries, and entries past a sequence's lengths, are left as they
+ * were. o (device, may be NULL): the output as sage2_attn_fwd writes it, or nothing when NULL.
+ * At least one of s_out and p8_out must be given; SAGE2_NO_FP32_FOLD is rejected. */
+sage2_status sage2_debug_attn_tiles(const sage2_params* p, const void* ws, size_t ws_bytes,
+                                    int32_t q_begin, int32_t q_count, int32_t* s_out,
+                                    uint8_t* p8_out, void* o, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ NO_K_SMOOTH, NO_Q_SMOOTH, PER_BLOCK_SCALES, NO_FP32_FOLD = 1, 2, 4, 8  # sage2_f
 
 # Symbols the header declares; tests check that the library exports every one.
 EXPORTS = ("sage2_workspace_size", "sage2_quantize_smooth", "sage2_attn_fwd", "sage2_status_string",
-           "sage2_workspace_layout", "sage2_debug_qk_i32")
+           "sage2_workspace_layout", "sage2_debug_attn_tiles")
 
 
 class Params(ctypes.Structure):
@@ -75,9 +75,9 @@ def lib():
         L.sage2_status_string.argtypes = [ctypes.c_int]
         L.sage2_status_string.restype = ctypes.c_char_p
         L.sage2_workspace_layout.argtypes = [PP, ctypes.POINTER(WsLayout)]
-        L.sage2_debug_qk_i32.argtypes = [PP, P, S, ctypes.c_int32, ctypes.c_int32, P, P]
+        L.sage2_debug_attn_tiles.argtypes = [PP, P, S, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
         for f in ("sage2_workspace_size", "sage2_quantize_smooth", "sage2_attn_fwd",
-                  "sage2_workspace_layout", "sage2_debug_qk_i32"):
+                  "sage2_workspace_layout", "sage2_debug_attn_tiles"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,10 +185,16 @@ def attn_fwd(p: Params, ws, o, stream=None):
                                 o.data_ptr(), _stream_ptr(stream)), "sage2_attn_fwd")
 
 
-def debug_qk_i32(p: Params, ws, q_begin: int, q_count: int, s_out, stream=None):
-    _check(lib().sage2_debug_qk_i32(ctypes.byref(p), ws.data_ptr(), ws.numel() * ws.element_size(),
-                                    int(q_begin), int(q_count), s_out.data_ptr(),
-                                    _stream_ptr(stream)), "sage2_debug_qk_i32")
+def debug_attn_tiles(p: Params, ws, q_begin: int, q_count: int, s_out=None, p8_out=None, o=None,
+                     stream=None):
+    """Runs the attention kernel with its tile dump (sage2_debug_attn_tiles): INT32 S into s_out and
+    P~ codes into p8_out ([B, H_q, q_count, N_kv] int32 / uint8 device tensors, either may be None),
+    the output into o when given."""
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(lib().sage2_debug_attn_tiles(ctypes.byref(p), ws.data_ptr(),
+                                        ws.numel() * ws.element_size(), int(q_begin), int(q_count),
+                                        ptr(s_out), ptr(p8_out), ptr(o), _stream_ptr(stream)),
+           "sage2_debug_attn_tiles")
 
 
 def attention(q, k, v, causal: bool = False, sm_scale: float = 0.0, out_dtype=None,

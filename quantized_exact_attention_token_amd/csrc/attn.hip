@@ -223,7 +223,10 @@ __device__ inline v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
 // NOFOLD = 1 is the ablation without the two-level accumulation: the output accumulates across
 // tiles inside the FP8 MFMA (rescaled by alpha in registers each tile), which on gfx950 adds its C
 // input with less than FP32 precision.
-template <int D, int CAUSAL, int OUT, int NOFOLD>
+// DUMP = 1 (tests only) also writes, for the rows of KArgs::dbg_*, the INT32 S of every key tile the
+// wave computes (from the same LDS-staged operands and MFMAs) and the e4m3 P~ codes it feeds to the
+// P~V MFMA; with a.o null it writes no output.
+template <int D, int CAUSAL, int OUT, int NOFOLD, int DUMP = 0>
 __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   constexpr int NC6 = D / 64;   // fp6 MFMAs per 32-key subtile (64 channels each)
   constexpr int NCB = D / 32;   // 32-channel blocks of the output
@@ -248,6 +251,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const int64_t prow = (int64_t)h * a.lay.q_rows + s.q_row0 + i;
   const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
   const int koff = s.kv_len - s.q_len;
+  // tile dump (tests only): this lane's row, when it is one of the dumped rows
+  const bool dump_row = DUMP && i < s.q_len && i >= a.dbg_q0 && i < a.dbg_q0 + a.dbg_qn;
+  const int64_t dump_at = DUMP ? (((int64_t)b * a.Hq + h) * a.dbg_qn + (i - a.dbg_q0)) * a.Nkv : 0;
 
   v8i qop[NC6];
   {
@@ -332,6 +338,15 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
           const uint8_t* kr = st + S::K_OFF + (32 * sub + n) * S::CB + 24 * hh;
           acc = mfma_fp6(load_fp6_op(kr), qop[0], acc);
         }
+        if constexpr (DUMP) {
+          if (dump_row && a.dbg_s) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = t * kBN + 32 * sub + 8 * (r >> 2) + 4 * hh + (r & 3);
+              if (key < s.kv_len) a.dbg_s[dump_at + key] = (int32_t)acc[r];
+            }
+          }
+        }
         const float cs = cq * sks[2 * sub + hh];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
@@ -386,6 +401,15 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
         const int w = cvt_fp8x2(x[4 * q], x[4 * q + 1], __float_as_int(x[4 * q]), false);
         pop[q >> 3][q & 7] = cvt_fp8x2(x[4 * q + 2], x[4 * q + 3], w, true);
       }
+      if constexpr (DUMP) {
+        if (dump_row && a.dbg_p8) {
+#pragma unroll
+          for (int k = 0; k < 64; ++k) {
+            const int key = t * kBN + 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * hh + (k & 3);
+            if (key < s.kv_len) a.dbg_p8[dump_at + key] = (uint8_t)(pop[k >> 5][(k >> 2) & 7] >> (8 * (k & 3)));
+          }
+        }
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         v16f inner = v16f{};
@@ -420,6 +444,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
 
   lsum += __shfl_xor(lsum, 32, 64);
   if (i >= s.q_len) return;
+  if (DUMP && a.o == nullptr) return;
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
   const float* svp = ws_ptr<float>(a, a.lay.sv) + ((int64_t)b * a.Hkv + g) * D;
   constexpr int ES = OUT == SAGE2_F32 ? 4 : 2;
@@ -437,62 +462,21 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   }
 }
 
-// Test-only: the same fp6 MFMA path, dumping S for rows [dbg_q0, dbg_q0 + dbg_qn).
-template <int D>
-__global__ __launch_bounds__(256) void k_debug_qk(KArgs a) {
-  constexpr int NC6 = D / 64;
-  constexpr int CB = 3 * D / 4;
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
-  if (qb * kQBlock + kQBlock <= a.dbg_q0 || qb * kQBlock >= a.dbg_q0 + a.dbg_qn) return;
-  const Seq s = load_seq(a, b);
-  const bool blk_ok = qb * kQBlock < s.q_len;
-  const int g = h / (a.Hq / a.Hkv);
-  const int i = qb * kQBlock + 32 * wave + n;
-  const bool row_out = i >= a.dbg_q0 && i < a.dbg_q0 + a.dbg_qn;
-  const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
-  v8i qop[NC6];
-#pragma unroll
-  for (int cb = 0; cb < NC6; ++cb) qop[cb] = v8i{};
-  if (blk_ok) {
-    const uint8_t* qrow = ws_ptr<uint8_t>(a, a.lay.qcode) + ((int64_t)h * a.lay.q_rows + s.q_row0 + i) * CB + hh * (CB / 2);
-#pragma unroll
-    for (int cb = 0; cb < NC6; ++cb) qop[cb] = load_fp6_op(qrow + 24 * cb);
-  }
-  const uint8_t* kcode = ws_ptr<uint8_t>(a, a.lay.kcode) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * CB;
-  int32_t* out = a.dbg_out + (((int64_t)b * a.Hq + h) * a.dbg_qn + (i - a.dbg_q0)) * a.Nkv;
-  const int nsub = (a.Nkv + 31) / 32;
-  for (int sub = 0; sub < nsub; ++sub) {
-    const int key0 = 32 * sub;
-    v16f acc = v16f{};
-    if (blk_ok && key0 < kvpad) {
-      const uint8_t* krow = kcode + (int64_t)(key0 + n) * CB + hh * (CB / 2);
-#pragma unroll
-      for (int cb = 0; cb < NC6; ++cb) acc = mfma_fp6(load_fp6_op(krow + 24 * cb), qop[cb], acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (row_out && key < a.Nkv) out[key] = (i < s.q_len && key < s.kv_len) ? (int32_t)acc[r] : 0;
-    }
-  }
-}
-
-template <int D, int CAUSAL, int NOFOLD>
+template <int D, int CAUSAL, int NOFOLD, int DUMP>
 int launch_attn_f(const KArgs& a, hipStream_t st) {
   const dim3 grid((a.Nq + kQBlock - 1) / kQBlock * a.Hq, a.B);
   switch (a.out_dtype) {
-    case SAGE2_F32: k_attn<D, CAUSAL, SAGE2_F32, NOFOLD><<<grid, 256, 0, st>>>(a); break;
-    case SAGE2_BF16: k_attn<D, CAUSAL, SAGE2_BF16, NOFOLD><<<grid, 256, 0, st>>>(a); break;
-    default: k_attn<D, CAUSAL, SAGE2_F16, NOFOLD><<<grid, 256, 0, st>>>(a); break;
+    case SAGE2_F32: k_attn<D, CAUSAL, SAGE2_F32, NOFOLD, DUMP><<<grid, 256, 0, st>>>(a); break;
+    case SAGE2_BF16: k_attn<D, CAUSAL, SAGE2_BF16, NOFOLD, DUMP><<<grid, 256, 0, st>>>(a); break;
+    default: k_attn<D, CAUSAL, SAGE2_F16, NOFOLD, DUMP><<<grid, 256, 0, st>>>(a); break;
   }
   return (int)hipGetLastError();
 }
 
 template <int D, int CAUSAL>
 int launch_attn_d(const KArgs& a, hipStream_t st) {
-  return (a.flags & SAGE2_NO_FP32_FOLD) ? launch_attn_f<D, CAUSAL, 1>(a, st)
-                                        : launch_attn_f<D, CAUSAL, 0>(a, st);
+  return (a.flags & SAGE2_NO_FP32_FOLD) ? launch_attn_f<D, CAUSAL, 1, 0>(a, st)
+                                        : launch_attn_f<D, CAUSAL, 0, 0>(a, st);
 }
 
 }  // namespace
@@ -504,13 +488,12 @@ int launch_attn(const KArgs& a, void* stream) {
   return a.causal ? launch_attn_d<128, 1>(a, st) : launch_attn_d<128, 0>(a, st);
 }
 
-int launch_debug_qk(const KArgs& a, void* stream) {
+int launch_attn_dump(const KArgs& a, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const dim3 grid((a.Nq + kQBlock - 1) / kQBlock, a.Hq, a.B);
-  if (a.d == 64) k_debug_qk<64><<<grid, 256, 0, st>>>(a);
-  else k_debug_qk<128><<<grid, 256, 0, st>>>(a);
-  return (int)hipGetLastError();
+  // the two-level (production) form only
+  if (a.d == 64) return a.causal ? launch_attn_f<64, 1, 0, 1>(a, st) : launch_attn_f<64, 0, 0, 1>(a, st);
+  return a.causal ? launch_attn_f<128, 1, 0, 1>(a, st) : launch_attn_f<128, 0, 0, 1>(a, st);
 }
 
 }  // namespace sage2

@@ -212,18 +212,22 @@ sage2_status sage2_attn_fwd(const sage2_params* p, const void* ws, size_t ws_byt
   return launch_attn(a, stream) == 0 ? SAGE2_OK : SAGE2_ERR_HIP;
 }
 
-sage2_status sage2_debug_qk_i32(const sage2_params* p, const void* ws, size_t ws_bytes,
-                                int32_t q_begin, int32_t q_count, int32_t* s_out, void* stream) {
+sage2_status sage2_debug_attn_tiles(const sage2_params* p, const void* ws, size_t ws_bytes,
+                                    int32_t q_begin, int32_t q_count, int32_t* s_out,
+                                    uint8_t* p8_out, void* o, void* stream) {
   sage2_status st = validate(p);
   if (st != SAGE2_OK) return st;
-  if (!s_out) return SAGE2_ERR_NULL;
+  if (!s_out && !p8_out) return SAGE2_ERR_NULL;
+  if (p->flags & SAGE2_NO_FP32_FOLD) return SAGE2_ERR_UNSUPPORTED;
   if (q_begin < 0 || q_count <= 0 || (int64_t)q_begin + q_count > p->N_q) return SAGE2_ERR_SHAPE;
+  if (o && !aligned16(o)) return SAGE2_ERR_ALIGN;
   if ((st = check_ws(p, ws, ws_bytes)) != SAGE2_OK) return st;
   KArgs a;
   fill_args(p, &a);
   a.ws = (char*)ws;
-  a.dbg_q0 = q_begin; a.dbg_qn = q_count; a.dbg_out = s_out;
-  return launch_debug_qk(a, stream) == 0 ? SAGE2_OK : SAGE2_ERR_HIP;
+  a.o = o;
+  a.dbg_q0 = q_begin; a.dbg_qn = q_count; a.dbg_s = s_out; a.dbg_p8 = p8_out;
+  return launch_attn_dump(a, stream) == 0 ? SAGE2_OK : SAGE2_ERR_HIP;
 }
 
 }  // extern "C"

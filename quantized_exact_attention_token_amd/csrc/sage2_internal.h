@@ -29,14 +29,17 @@ struct KArgs {
   const int32_t *cu_q, *cu_kv;
   char* ws;
   sage2_ws_layout lay;
-  // debug dump
+  // test-only dump of the attention kernel's own tiles (rows [dbg_q0, dbg_q0 + dbg_qn) of every
+  // sequence and q head): INT32 S and e4m3 P~ codes, [B][Hq][dbg_qn][Nkv]; either may be null
   int32_t dbg_q0, dbg_qn;
-  int32_t* dbg_out;
+  int32_t* dbg_s;
+  uint8_t* dbg_p8;
 };
 
 // Launchers (defined in the .hip files). Return hipSuccess as 0, else the HIP error code.
 int launch_prepass(const KArgs& a, void* stream);
 int launch_attn(const KArgs& a, void* stream);
-int launch_debug_qk(const KArgs& a, void* stream);
+// the attention kernel with the tile dump of KArgs::dbg_* (a.o may be null: no output is written)
+int launch_attn_dump(const KArgs& a, void* stream);
 
 }  // namespace sage2

@@ -118,7 +118,7 @@ def test_null_pointers(lib):
     assert lib.sage2_quantize_smooth(ctypes.byref(p), None, 256, 256, 256, 1 << 30, None) == sage2.ERR_NULL
     assert lib.sage2_attn_fwd(ctypes.byref(p), 256, 1 << 30, None, None) == sage2.ERR_NULL
     assert lib.sage2_attn_fwd(ctypes.byref(p), None, 1 << 30, 256, None) == sage2.ERR_NULL
-    assert lib.sage2_debug_qk_i32(ctypes.byref(p), 256, 1 << 30, 0, 1, None, None) == sage2.ERR_NULL
+    assert lib.sage2_debug_attn_tiles(ctypes.byref(p), 256, 1 << 30, 0, 1, None, None, None, None) == sage2.ERR_NULL
 
 
 def test_alignment_and_workspace_checks(lib):
@@ -130,8 +130,12 @@ def test_alignment_and_workspace_checks(lib):
     assert lib.sage2_quantize_smooth(ctypes.byref(p), 0x1000, 0x2000, 0x3000, 0x10000, need - 1, None) == sage2.ERR_WORKSPACE
     assert lib.sage2_attn_fwd(ctypes.byref(p), 0x10000, need - 256, 0x1000, None) == sage2.ERR_WORKSPACE
     assert lib.sage2_attn_fwd(ctypes.byref(p), 0x10000, need, 0x1004, None) == sage2.ERR_ALIGN
-    assert lib.sage2_debug_qk_i32(ctypes.byref(p), 0x10000, need, 250, 100, 0x1000, None) == sage2.ERR_SHAPE
-    assert lib.sage2_debug_qk_i32(ctypes.byref(p), 0x10000, need, -1, 10, 0x1000, None) == sage2.ERR_SHAPE
+    dbg = lib.sage2_debug_attn_tiles
+    assert dbg(ctypes.byref(p), 0x10000, need, 250, 100, 0x1000, None, None, None) == sage2.ERR_SHAPE
+    assert dbg(ctypes.byref(p), 0x10000, need, -1, 10, None, 0x1000, None, None) == sage2.ERR_SHAPE
+    assert dbg(ctypes.byref(p), 0x10000, need, 0, 10, 0x1000, None, 0x1008, None) == sage2.ERR_ALIGN
+    pf = _params(flags=sage2.NO_FP32_FOLD)
+    assert dbg(ctypes.byref(pf), 0x10000, need, 0, 10, 0x1000, None, None, None) == sage2.ERR_UNSUPPORTED
 
 
 def _varlen(lib, cu_q, cu_kv, Nq=None, Nkv=None, drop=None):
@@ -187,4 +191,3 @@ def test_rejects_layouts_past_int32(lib):
     assert _ws_status(lib, p)[0] == sage2.ERR_SHAPE
     p.B = 1   # 1563 * 200064 = 3.1e8 entries per head: fine
     assert _ws_status(lib, p)[0] == sage2.OK
-
