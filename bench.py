@@ -9,7 +9,9 @@ with the inputs already resident in HBM. Prints one JSON line.
 
 value = attention ops (4*Nq*Nkv*d per sequence and q head, halved under a causal mask) per second
 of the whole step; `kernel_tops` is the same count over sage2_attn_fwd alone (the kernel-only
-figure); `roofline` prices the attention kernel against the dense int8/fp8 MFMA peak.
+figure) and `kernel_frac_of_peak` its fraction of the dense int8/fp8 MFMA peak (the metric's
+denominator). `roofline` prices the attention kernel at the peaks of the MFMA data types it runs:
+half of its ops (the INT4 Q K^T, carried in e2m3) on the fp6 MFMA and half (P~V) on the fp8 MFMA.
 """
 from __future__ import annotations
 
@@ -26,7 +28,11 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "attention TOPS at d=128 N=4K-32K (1 GPU), % of i8/fp8 MFMA peak; err vs oracle"
 PEAK_TOPS = 5000.0          # MI355X dense int8 (and fp8) MFMA peak, TOPS
-NOMINAL_MHZ = 2400.0        # the engine clock that peak is quoted at
+PEAK_FP6_TOPS = 10100.0     # MI355X dense fp6 / fp4 MFMA peak
+# half of the kernel's ops on each: the time bound is (ops/2)/PEAK_FP6 + (ops/2)/PEAK_FP8, so the
+# effective peak of the mix is the harmonic mean of the two
+PEAK_MIXED_TOPS = 1.0 / (0.5 / PEAK_FP6_TOPS + 0.5 / PEAK_TOPS)
+NOMINAL_MHZ = 2400.0        # the engine clock the peaks are quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_gqa16k_traffic.json")
 
 
@@ -100,11 +106,14 @@ def cpu_baseline(run, w, budget_s: float = 20.0):
     import oracle as O
     import gpu_harness as H
 
-    threads = min(os.cpu_count() or 1, 16)
+    host_cpus = os.cpu_count() or 1
+    threads = min(host_cpus, 16)  # the GPU machine gives one GPU's job a 16-CPU share
     grp = w.Hq // w.Hkv
+    import torch
     out = run.out_seq(0)
+    out32 = run.out_seq(0, run.attn_as(torch.float32))
     t_tot = ops_tot = 0.0
-    errs, gpus, refs = [], [], []
+    errs, errs32, gpus, refs = [], [], [], []
     ng = 0
     nrows = 0
     t_group = 0.0
@@ -134,16 +143,25 @@ def cpu_baseline(run, w, budget_s: float = 20.0):
         # 1e-2 + the allowance for FP8 roundings of P~ within the kernel's arithmetic error of a
         # boundary + half an ulp of the output format
         gpu = out[ng * grp:(ng + 1) * grp, rows]
-        errs.append((np.abs(gpu - ref), H.MAX_ABS_TOL + allow + H.half_ulp(ref, w.dtype)))
+        base = H.MAX_ABS_TOL + H.half_ulp(ref, w.dtype)
+        errs.append((np.abs(gpu - ref), base + allow, base, allow))
+        # the same rows from an f32 output of the same workspace: the bare 1e-2 bound (+ allowance)
+        g32 = out32[ng * grp:(ng + 1) * grp, rows]
+        errs32.append((np.abs(g32 - ref), H.MAX_ABS_TOL + H.half_ulp(ref, torch.float32) + allow))
         gpus.append(gpu)
         refs.append(ref)
         ng += 1
     tops = ops_tot / t_tot / 1e12
-    e = np.concatenate([a.ravel() for a, _ in errs])
-    tol = np.concatenate([b.ravel() for _, b in errs])
+    cat = lambda xs, i: np.concatenate([x[i].ravel() for x in xs])
+    e, tol, base, allow = cat(errs, 0), cat(errs, 1), cat(errs, 2), cat(errs, 3)
+    e32, tol32 = cat(errs32, 0), cat(errs32, 1)
     err = {"max_abs": float(e.max()), "max_abs_beyond_tolerance": float(max(0.0, (e - tol).max())),
            "within_tolerance": bool((e <= tol).all()),
            "cos": H.cos(np.concatenate([g.ravel() for g in gpus]), np.concatenate([r.ravel() for r in refs])),
+           "allow_max": float(allow.max()), "n_needed_allowance": int((e > base).sum()),
+           "tolerance": "1e-2 + half an ulp of the output dtype at the value + the P~ allowance",
+           "f32_output": {"max_abs": float(e32.max()), "within_tolerance": bool((e32 <= tol32).all()),
+                          "n_beyond_bare_1e-2": int((e32 > H.MAX_ABS_TOL).sum())},
            "rows": int(nrows), "heads": int(ng * grp)}
     q, k, v = q0, k0, v0
     # the oracle's plain FP64 attention on a slice of the same rows (about 2 s of work)
@@ -165,7 +183,14 @@ def cpu_baseline(run, w, budget_s: float = 20.0):
     t0 = time.perf_counter()
     O.attn_quant(O.quantize(tq, tk, tv, nthreads=1), tw.causal, nthreads=1)
     t_tiny = time.perf_counter() - t0
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
     return ({"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
+             "host_cpus": host_cpus, "thread_cap": 16, "cpu_model": model,
              "sample": f"kv heads 0..{ng - 1} with their {ng * grp} q heads: the full pre-pass of "
                        f"each group, then attention for {nrows} evenly spaced query rows per head; "
                        f"ops counted for those rows only, time = pre-pass + rows ({t_tot:.1f}s)",
@@ -289,8 +314,11 @@ def main():
     # after the timed steps); the peak scales with it
     clock = None if args.no_clock else gfx_clock_under_load(run.attn)
     traffic = traffic_per_launch(w.name)
-    roofline = {"bound": "mfma", "achieved": kernel_tops, "peak": PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": kernel_tops / PEAK_TOPS, "traffic": traffic,
+    roofline = {"bound": "mfma", "achieved": kernel_tops, "peak": PEAK_MIXED_TOPS, "unit": "TFLOP/s",
+                "frac": kernel_tops / PEAK_MIXED_TOPS, "traffic": traffic,
+                "peak_note": "half of the ops (INT4 QK^T carried in e2m3) at the dense fp6 MFMA peak "
+                             "10.1 PF/s, half (P~V) at the dense fp8 peak 5.0 PF/s: harmonic mean",
+                "frac_of_i8_fp8_peak": kernel_tops / PEAK_TOPS,
                 "kernel": "k_attn (sage2_attn_fwd)",
                 "limiter": "VALU issue: the online softmax's per-element arithmetic (dequantize, max, "
                            "exp, row sum, fp8 conversion, fold), not the MFMA",
@@ -300,7 +328,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8/fp8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4(e2m3)/fp8", "data": "synthetic",
         "config": {"workload": f"{w.name}: {'causal ' if w.causal else ''}"
                                f"{'GQA ' if w.Hq != w.Hkv else ''}B{w.B} Hq{w.Hq} Hkv{w.Hkv} "
                                f"N{w.Nq} d{w.d} {str(w.dtype).split('.')[-1]}",
