@@ -124,9 +124,12 @@ typedef struct {
  *                                             tile, channel c, half h, slot s holds key
  *                                             32*(s/16) + 8*((s%16)/4) + 4*h + s%4
  *   delta      f32   [H_q][delta_len]         correction (qbar . smoothed k_j) * sm_scale * log2(e),
- *                                             per sequence a [q_blocks][kv_rows] block at delta0;
- *                                             entries of keys a causal mask hides from every row
- *                                             of the Q block are unspecified
+ *                                             per sequence one row per Q block from delta0: all
+ *                                             kv_rows keys without a causal mask; with one, row qb
+ *                                             holds keys [0, V(qb)), V(qb) = the block's last
+ *                                             visible key + 1 rounded up to 128 (the last block:
+ *                                             all kv_rows), rows back to back; entries of keys the
+ *                                             mask hides from every row of the block are unspecified
  */
 typedef struct {
   int64_t total_bytes;

@@ -249,7 +249,6 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const int g = h / (a.Hq / a.Hkv);
   const int i = qb * kQBlock + 32 * wave + n;  // this lane's query row within the sequence
   const int64_t prow = (int64_t)h * a.lay.q_rows + s.q_row0 + i;
-  const int kvpad = (s.kv_len + kKVPad - 1) / kKVPad * kKVPad;
   const int koff = s.kv_len - s.q_len;
   // tile dump (tests only): this lane's row, when it is one of the dumped rows
   const bool dump_row = DUMP && i < s.q_len && i >= a.dbg_q0 && i < a.dbg_q0 + a.dbg_qn;
@@ -277,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const float* skp = ws_ptr<float>(a, a.lay.sk) + (int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16;
   const uint8_t* v8 = ws_ptr<uint8_t>(a, a.lay.v8) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * D;
   const float* drow = ws_ptr<float>(a, a.lay.delta) + (int64_t)h * a.lay.delta_len + s.delta0 +
-                      (int64_t)qb * kvpad;
+                      delta_row_offset(CAUSAL, s.q_len, s.kv_len, qb);
 
   float m = kMaxFloor, lsum = 0.0f, ref = kMaxFloor - kLog2_448;
   v16f o[NCB];

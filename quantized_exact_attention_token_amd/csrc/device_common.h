@@ -25,7 +25,8 @@ __device__ inline Seq load_seq(const KArgs& a, int b) {
   if (!a.varlen) {
     const int nqb = (a.Nq + kQBlock - 1) / kQBlock;
     const int kvpad = (a.Nkv + kKVPad - 1) / kKVPad * kKVPad;
-    return Seq{0, a.Nq, 0, a.Nkv, b * nqb * kQBlock, b * kvpad, b * nqb, b * nqb * kvpad};
+    return Seq{0, a.Nq, 0, a.Nkv, b * nqb * kQBlock, b * kvpad, b * nqb,
+               (int32_t)(b * delta_seq_len(a.causal, a.Nq, a.Nkv))};
   }
   const int32_t* t = reinterpret_cast<const int32_t*>(a.ws + a.lay.seq_table) + b * kSeqCols;
   Seq s;

@@ -94,7 +94,7 @@ void compute_layout(const sage2_params* p, sage2_ws_layout* L) {
     L->q_rows += nqb * kQBlock;
     L->q_blocks += nqb;
     L->kv_rows += kvpad;
-    L->delta_len += nqb * kvpad;
+    L->delta_len += delta_seq_len(p->causal, lq, lkv);
   }
   int64_t off = 0;
   auto take = [&](int64_t bytes) {

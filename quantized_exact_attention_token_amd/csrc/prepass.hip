@@ -37,7 +37,7 @@ __global__ void k_plan(KArgs a) {
     int64_t kvpad = (lk + kKVPad - 1) / kKVPad * kKVPad;
     const bool ok = lq >= 0 && lk >= 0 && lq <= a.Nq && lk <= a.Nkv &&
                     q_row + nqb * kQBlock <= a.lay.q_rows && kv_row + kvpad <= a.lay.kv_rows &&
-                    delta + nqb * kvpad <= a.lay.delta_len;
+                    delta + delta_seq_len(a.causal, lq, lk) <= a.lay.delta_len;
     if (!ok) lq = lk = nqb = kvpad = 0;
     int32_t* r = t + b * kSeqCols;
     r[kQStart] = (int32_t)qs; r[kQLen] = (int32_t)lq;
@@ -47,7 +47,7 @@ __global__ void k_plan(KArgs a) {
     q_row += nqb * kQBlock;
     kv_row += kvpad;
     qblk += nqb;
-    delta += nqb * kvpad;
+    delta += delta_seq_len(a.causal, lq, lk);
   }
 }
 
@@ -515,7 +515,7 @@ struct DeltaItem {
   const float* qbar;
   float* delta;
   float L;
-  int t, g, grp, qbmin, nlive, koff, kvpad, li, lk;
+  int t, g, grp, qbmin, nlive, koff, li, lk;
 };
 
 // Correction values of 32 pairs (from p0) x 32 NKB keys (from key k0 of the tile): NKB f32 MFMA
@@ -567,7 +567,8 @@ __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
     // last key that any row of Q block qb sees
     int jm = c.s.kv_len - 1;
     if (c.a.causal) jm = min(jm, min(c.s.q_len, (qb + 1) * kQBlock) - 1 + c.koff);
-    float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 + (int64_t)qb * c.kvpad;
+    float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 +
+                  delta_row_offset(c.a.causal, c.s.q_len, c.s.kv_len, qb);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int j = c.t * kKVTile + k0 + 32 * kb + c.li;
@@ -635,7 +636,7 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   // splits each block's keys in two halves instead, so that up to twice as many waves have work
   const int nlive = (nqb - qbmin) * grp;
   const int nblk = (nlive + 31) / 32;
-  const DeltaItem it{a, s, kt, qbar, delta, a.L, t, g, grp, qbmin, nlive, koff, kvpad, li, lk};
+  const DeltaItem it{a, s, kt, qbar, delta, a.L, t, g, grp, qbmin, nlive, koff, li, lk};
   if (nblk >= 4) {
     for (int w = wave; w < nblk; w += 4) delta_item<D, 2>(it, 32 * w, 0);
   } else {

@@ -16,6 +16,46 @@ constexpr int kSeqCols = 8;    // int32 columns of a sequence-table row
 // Columns of the per-sequence table the plan kernel writes into the workspace.
 enum SeqCol { kQStart = 0, kQLen, kKVStart, kKVLen, kQRow0, kKVRow0, kQBlk0, kDelta0 };
 
+// Layout helpers shared by the host (workspace sizes) and the kernels (offsets).
+#if defined(__HIPCC__)
+#define SAGE2_HD __host__ __device__
+#else
+#define SAGE2_HD
+#endif
+
+// Smallest multiple of 128 that is >= x (x may be negative).
+SAGE2_HD inline int64_t ceil128(int64_t x) { return x >= 0 ? (x + 127) / 128 * 128 : -((-x) / 128 * 128); }
+
+// sum over b in [0, n) of min(K, max(0, 128 (b + 1) + c)), for c and K multiples of 128, K >= 0.
+SAGE2_HD inline int64_t clamped_ramp_sum(int64_t n, int64_t c, int64_t K) {
+  if (n <= 0) return 0;
+  int64_t b0 = -c / 128;            // first b whose term is > 0
+  if (b0 < 0) b0 = 0;
+  int64_t b1 = (K - c) / 128 - 1;   // first b whose term is >= K
+  if (b1 < b0) b1 = b0;
+  const int64_t lo = b0 < n ? b0 : n, hi = b1 < n ? b1 : n;
+  return 64 * (hi * (hi + 1) - lo * (lo + 1)) + c * (hi - lo) + (n - hi) * K;
+}
+
+// The correction table of one sequence (q_len queries, kv_len keys) is one row per 128-query block.
+// Without a causal mask every row holds all kv_len keys rounded up to 128. With one, row qb holds
+// only the keys [0, V(qb)), V(qb) = the block's last visible key + 1 rounded up to 128 (0 if it sees
+// none): the attention kernel visits no other key tile, and the table shrinks to about half. For
+// every block but the last, V(qb) = clamp(128 (qb + 1) + ceil128(kv_len - q_len), 0, kvpad); the
+// last block sees every key.
+// Offset of row qb within the sequence's table (qb <= number of blocks):
+SAGE2_HD inline int64_t delta_row_offset(int causal, int64_t q_len, int64_t kv_len, int64_t qb) {
+  const int64_t kvpad = ceil128(kv_len);
+  if (!causal) return qb * kvpad;
+  const int64_t nqb = (q_len + 127) / 128;
+  if (qb >= nqb) return nqb == 0 ? 0 : clamped_ramp_sum(nqb - 1, ceil128(kv_len - q_len), kvpad) + kvpad;
+  return clamped_ramp_sum(qb, ceil128(kv_len - q_len), kvpad);
+}
+// Entries of the sequence's whole table.
+SAGE2_HD inline int64_t delta_seq_len(int causal, int64_t q_len, int64_t kv_len) {
+  return delta_row_offset(causal, q_len, kv_len, (q_len + 127) / 128);
+}
+
 // Everything a kernel needs, passed by value.
 struct KArgs {
   int32_t B, Hq, Hkv, Nq, Nkv, causal, in_dtype, out_dtype, varlen;

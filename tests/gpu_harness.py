@@ -109,7 +109,8 @@ class GpuRun:
             # no table without cu_seqlens: sequence b sits after b full sequences
             nqb_, kvpad_ = (w.Nq + 127) // 128, (w.Nkv + 127) // 128 * 128
             qs, lq, ks, lk = 0, w.Nq, 0, w.Nkv
-            qrow0, kvrow0, qblk0, delta0 = b * nqb_ * 128, b * kvpad_, b * nqb_, b * nqb_ * kvpad_
+            qrow0, kvrow0, qblk0 = b * nqb_ * 128, b * kvpad_, b * nqb_
+            delta0 = b * sum(delta_row_keys(w.causal, w.Nq, w.Nkv))
         else:
             tab = ws[lay.seq_table:lay.seq_table + 4 * 8 * self.p.B].view(np.int32).reshape(-1, 8)
             qs, lq, ks, lk, qrow0, kvrow0, qblk0, delta0 = (int(x) for x in tab[b])
@@ -158,7 +159,13 @@ class GpuRun:
                 canon[:, key::64, :] = v8[:, :, :, h, s]
         out["v8"] = canon[:, :lk]
         dl = arr(lay.delta, np.float32, Hq * lay.delta_len).reshape(Hq, lay.delta_len)
-        out["delta"] = dl[:, delta0:delta0 + nqb * kvpad].reshape(Hq, nqb, kvpad)[:, :, :lk]
+        # one row per Q block, back to back; keys past a row's stored range read as NaN
+        full = np.full((Hq, nqb, kvpad), np.nan, np.float32)
+        at = delta0
+        for qb, n in enumerate(delta_row_keys(w.causal, lq, lk)):
+            full[:, qb, :n] = dl[:, at:at + n]
+            at += n
+        out["delta"] = full[:, :, :lk]
         if dt < d:
             for name in ("kbar", "sv", "qbar", "qcode", "qcode_pad", "kcode", "v8"):
                 pad = out[name][..., dt:]
@@ -191,6 +198,20 @@ class GpuRun:
         else:
             o = o[int(self.cu_cpu[b]):int(self.cu_cpu[b + 1])]
         return o.permute(1, 0, 2).double().numpy()
+
+
+def delta_row_keys(causal: bool, lq: int, lk: int) -> list:
+    """Keys stored per Q block in the correction table of one sequence: all keys rounded up to 128
+    without a causal mask; with one, the block's last visible key + 1 rounded up to 128."""
+    kvpad = (lk + 127) // 128 * 128
+    rows = []
+    for qb in range((lq + 127) // 128):
+        if not causal:
+            rows.append(kvpad)
+            continue
+        last = min(lq, 128 * (qb + 1)) - 1 + (lk - lq)  # last visible key of the block
+        rows.append(min(kvpad, max(0, (last + 1 + 127) // 128 * 128)))
+    return rows
 
 
 def half_ulp(ref: np.ndarray, dtype) -> np.ndarray:

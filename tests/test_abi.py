@@ -50,9 +50,12 @@ def test_workspace_size_closed_form(lib):
     assert st == sage2.OK
     lay = sage2.workspace_layout(_params())
     assert lay.total_bytes == n
-    # per sequence: Q rows padded to 384 (3 blocks), K/V rows to 512
-    assert (lay.q_rows, lay.kv_rows, lay.q_blocks, lay.delta_len) == (768, 1024, 6, 2 * 3 * 512)
-    assert n >= 8 * 768 * 64 + 2 * 1024 * 64 + 2 * 1024 * 128 + 8 * 3072 * 4
+    # per sequence: Q rows padded to 384 (3 blocks), K/V rows to 512; causal correction rows of
+    # 384 (block 0 sees keys up to 127 + 200), 512, 512 keys
+    assert (lay.q_rows, lay.kv_rows, lay.q_blocks, lay.delta_len) == (768, 1024, 6, 2 * (384 + 512 + 512))
+    assert n >= 8 * 768 * 64 + 2 * 1024 * 64 + 2 * 1024 * 128 + 8 * 2816 * 4
+    full = sage2.workspace_layout(_params(causal=0))
+    assert full.delta_len == 2 * 3 * 512
     offs = [lay.seq_table, lay.k_partial, lay.v_partial, lay.kbar, lay.sv, lay.sv_inv, lay.qbar,
             lay.qcode, lay.sq, lay.kcode, lay.sk, lay.v8, lay.delta]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
@@ -183,7 +186,7 @@ def test_status_strings(lib):
 def test_rejects_layouts_past_int32(lib):
     """Per-head workspace extents are carried as int32 on the device: a dense shape whose correction
     table would pass 2^31 - 1 entries per head is refused before any sizing overflow."""
-    p = _params(N_q=200_000, N_kv=200_000, B=8)   # 8 * 1563 Q blocks * 200064 keys > 2^31
+    p = _params(N_q=200_000, N_kv=200_000, B=8, causal=0)   # 8 * 1563 Q blocks * 200064 keys > 2^31
     for name in ("q_stride", "o_stride"):
         getattr(p, name)[:] = (200_000 * 8 * 128, 8 * 128, 128)
     for name in ("k_stride", "v_stride"):
@@ -191,3 +194,37 @@ def test_rejects_layouts_past_int32(lib):
     assert _ws_status(lib, p)[0] == sage2.ERR_SHAPE
     p.B = 1   # 1563 * 200064 = 3.1e8 entries per head: fine
     assert _ws_status(lib, p)[0] == sage2.OK
+    p.B, p.causal = 8, 1   # causal: about half the table, 1.25e9 entries: fine
+    assert _ws_status(lib, p)[0] == sage2.OK
+    p.B = 16               # 2.5e9: refused
+    assert _ws_status(lib, p)[0] == sage2.ERR_SHAPE
+
+
+def test_causal_correction_rows_match_a_plain_loop(lib):
+    """The compact causal correction-table length (a closed form in the library) equals the plain
+    per-block sum of the keys each Q block can see, rounded up to 128, on random dense and packed
+    shapes, including N_q != N_kv and empty sequences."""
+    import numpy as np
+    import gpu_harness as H
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        causal = int(rng.integers(2))
+        nseq = int(rng.integers(1, 5))
+        lq = [int(x) for x in rng.integers(0, 1200, nseq)]
+        lk = [int(x) for x in rng.integers(0, 1200, nseq)]
+        if rng.integers(2):  # dense
+            lq, lk = [max(1, lq[0])] * nseq, [max(1, lk[0])] * nseq
+            p = _params(B=nseq, N_q=lq[0], N_kv=lk[0], causal=causal)
+            keep = None
+        else:
+            cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+            ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+            keep = (cq, ck)
+            p = _params(B=nseq, N_q=max(1, max(lq)), N_kv=max(1, max(lk)), causal=causal)
+            p.cu_seqlens_q = p.cu_seqlens_kv = 0x1000  # device pointers: never dereferenced here
+            p.cu_seqlens_q_host = cq.ctypes.data
+            p.cu_seqlens_kv_host = ck.ctypes.data
+        lay = sage2.workspace_layout(p)
+        want = sum(sum(H.delta_row_keys(bool(causal), a, b)) for a, b in zip(lq, lk))
+        assert lay.delta_len == want, (causal, lq, lk, lay.delta_len, want)
+
