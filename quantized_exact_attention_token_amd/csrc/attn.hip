@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(KArgs a) {
   const float* skp = ws_ptr<float>(a, a.lay.sk) + (int64_t)g * (a.lay.kv_rows / 16) + s.kv_row0 / 16;
   const uint8_t* v8 = ws_ptr<uint8_t>(a, a.lay.v8) + ((int64_t)g * a.lay.kv_rows + s.kv_row0) * D;
   const float* drow = ws_ptr<float>(a, a.lay.delta) + (int64_t)h * a.lay.delta_len + s.delta0 +
-                      delta_row_offset(CAUSAL, s.q_len, s.kv_len, qb);
+                      DeltaRows(CAUSAL, s.q_len, s.kv_len).offset(qb);
 
   float m = kMaxFloor, lsum = 0.0f, ref = kMaxFloor - kLog2_448;
   v16f o[NCB];

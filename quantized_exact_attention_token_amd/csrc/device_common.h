@@ -26,7 +26,7 @@ __device__ inline Seq load_seq(const KArgs& a, int b) {
     const int nqb = (a.Nq + kQBlock - 1) / kQBlock;
     const int kvpad = (a.Nkv + kKVPad - 1) / kKVPad * kKVPad;
     return Seq{0, a.Nq, 0, a.Nkv, b * nqb * kQBlock, b * kvpad, b * nqb,
-               (int32_t)(b * delta_seq_len(a.causal, a.Nq, a.Nkv))};
+               b * DeltaRows(a.causal, a.Nq, a.Nkv).total(a.Nq)};
   }
   const int32_t* t = reinterpret_cast<const int32_t*>(a.ws + a.lay.seq_table) + b * kSeqCols;
   Seq s;

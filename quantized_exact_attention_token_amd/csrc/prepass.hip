@@ -35,9 +35,11 @@ __global__ void k_plan(KArgs a) {
     }
     int64_t nqb = (lq + kQBlock - 1) / kQBlock;
     int64_t kvpad = (lk + kKVPad - 1) / kKVPad * kKVPad;
-    const bool ok = lq >= 0 && lk >= 0 && lq <= a.Nq && lk <= a.Nkv &&
-                    q_row + nqb * kQBlock <= a.lay.q_rows && kv_row + kvpad <= a.lay.kv_rows &&
-                    delta + delta_seq_len(a.causal, lq, lk) <= a.lay.delta_len;
+    // (lengths within the bounds the host validated, so the table size fits in int)
+    const bool len_ok = lq >= 0 && lk >= 0 && lq <= a.Nq && lk <= a.Nkv;
+    const int64_t dlen = len_ok ? DeltaRows(a.causal, (int)lq, (int)lk).total((int)lq) : 0;
+    const bool ok = len_ok && q_row + nqb * kQBlock <= a.lay.q_rows &&
+                    kv_row + kvpad <= a.lay.kv_rows && delta + dlen <= a.lay.delta_len;
     if (!ok) lq = lk = nqb = kvpad = 0;
     int32_t* r = t + b * kSeqCols;
     r[kQStart] = (int32_t)qs; r[kQLen] = (int32_t)lq;
@@ -47,7 +49,7 @@ __global__ void k_plan(KArgs a) {
     q_row += nqb * kQBlock;
     kv_row += kvpad;
     qblk += nqb;
-    delta += delta_seq_len(a.causal, lq, lk);
+    delta += ok ? dlen : 0;
   }
 }
 
@@ -512,6 +514,7 @@ struct DeltaItem {
   const KArgs& a;
   const Seq& s;
   const float* kt;  // k~ tile in LDS, rows of D + 4 floats
+  DeltaRows rows;   // row offsets of the sequence's correction table
   const float* qbar;
   float* delta;
   float L;
@@ -567,8 +570,7 @@ __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
     // last key that any row of Q block qb sees
     int jm = c.s.kv_len - 1;
     if (c.a.causal) jm = min(jm, min(c.s.q_len, (qb + 1) * kQBlock) - 1 + c.koff);
-    float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 +
-                  delta_row_offset(c.a.causal, c.s.q_len, c.s.kv_len, qb);
+    float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 + c.rows.offset(qb);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int j = c.t * kKVTile + k0 + 32 * kb + c.li;
@@ -636,7 +638,8 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   // splits each block's keys in two halves instead, so that up to twice as many waves have work
   const int nlive = (nqb - qbmin) * grp;
   const int nblk = (nlive + 31) / 32;
-  const DeltaItem it{a, s, kt, qbar, delta, a.L, t, g, grp, qbmin, nlive, koff, li, lk};
+  const DeltaItem it{a, s, kt, DeltaRows(a.causal, s.q_len, s.kv_len), qbar, delta, a.L, t, g, grp,
+                     qbmin, nlive, koff, li, lk};
   if (nblk >= 4) {
     for (int w = wave; w < nblk; w += 4) delta_item<D, 2>(it, 32 * w, 0);
   } else {

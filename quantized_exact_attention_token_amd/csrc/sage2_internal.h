@@ -26,34 +26,45 @@ enum SeqCol { kQStart = 0, kQLen, kKVStart, kKVLen, kQRow0, kKVRow0, kQBlk0, kDe
 // Smallest multiple of 128 that is >= x (x may be negative).
 SAGE2_HD inline int64_t ceil128(int64_t x) { return x >= 0 ? (x + 127) / 128 * 128 : -((-x) / 128 * 128); }
 
-// sum over b in [0, n) of min(K, max(0, 128 (b + 1) + c)), for c and K multiples of 128, K >= 0.
-SAGE2_HD inline int64_t clamped_ramp_sum(int64_t n, int64_t c, int64_t K) {
-  if (n <= 0) return 0;
-  int64_t b0 = -c / 128;            // first b whose term is > 0
-  if (b0 < 0) b0 = 0;
-  int64_t b1 = (K - c) / 128 - 1;   // first b whose term is >= K
-  if (b1 < b0) b1 = b0;
-  const int64_t lo = b0 < n ? b0 : n, hi = b1 < n ? b1 : n;
-  return 64 * (hi * (hi + 1) - lo * (lo + 1)) + c * (hi - lo) + (n - hi) * K;
-}
-
 // The correction table of one sequence (q_len queries, kv_len keys) is one row per 128-query block.
-// Without a causal mask every row holds all kv_len keys rounded up to 128. With one, row qb holds
-// only the keys [0, V(qb)), V(qb) = the block's last visible key + 1 rounded up to 128 (0 if it sees
-// none): the attention kernel visits no other key tile, and the table shrinks to about half. For
-// every block but the last, V(qb) = clamp(128 (qb + 1) + ceil128(kv_len - q_len), 0, kvpad); the
-// last block sees every key.
-// Offset of row qb within the sequence's table (qb <= number of blocks):
-SAGE2_HD inline int64_t delta_row_offset(int causal, int64_t q_len, int64_t kv_len, int64_t qb) {
-  const int64_t kvpad = ceil128(kv_len);
-  if (!causal) return qb * kvpad;
-  const int64_t nqb = (q_len + 127) / 128;
-  if (qb >= nqb) return nqb == 0 ? 0 : clamped_ramp_sum(nqb - 1, ceil128(kv_len - q_len), kvpad) + kvpad;
-  return clamped_ramp_sum(qb, ceil128(kv_len - q_len), kvpad);
-}
-// Entries of the sequence's whole table.
-SAGE2_HD inline int64_t delta_seq_len(int causal, int64_t q_len, int64_t kv_len) {
-  return delta_row_offset(causal, q_len, kv_len, (q_len + 127) / 128);
+// Without a causal mask every row holds all kv_len keys rounded up to 128 (kvpad). With one, row qb
+// holds only the keys [0, V(qb)), V(qb) = the block's last visible key + 1 rounded up to 128 (0 if
+// it sees none): the attention kernel visits no other key tile, and the table shrinks to about half.
+// In units of 128 keys, every block but the last has V(qb)/128 = clamp(qb + 1 + c, 0, K), with
+// K = kvpad / 128 and c = ceil128(kv_len - q_len) / 128; the last block sees every key. So the row
+// offset of block qb is G(qb + c) - G(c) units, G(n) = sum over v = 1..n of min(v, K) (0 for n <= 0).
+// I is the integer type of the arithmetic: int64_t on the host (before any size is validated), int in
+// the kernels (the host refuses workspaces whose per-head table passes 2^31 - 1 entries, so every
+// offset and every G value, at most 2^24 units, fits).
+template <typename I>
+struct DeltaRowsT {
+  I kvpad, K, c, g0;
+  int causal;
+  SAGE2_HD static I G(I n, I K) {
+    const I np = n > 0 ? n : 0;
+    const I t = np < K ? np : K;
+    return t * (t + 1) / 2 + (np - t) * K;
+  }
+  SAGE2_HD DeltaRowsT(int causal_, I q_len, I kv_len) {
+    causal = causal_;
+    kvpad = (I)ceil128(kv_len);
+    K = kvpad / 128;
+    c = (I)(ceil128(kv_len - q_len) / 128);
+    g0 = G(c, K);
+  }
+  // offset of row qb within the sequence's table, for 0 <= qb < number of Q blocks
+  SAGE2_HD I offset(I qb) const { return causal ? 128 * (G(qb + c, K) - g0) : qb * kvpad; }
+  // entries of the sequence's whole table (the last block holds every key)
+  SAGE2_HD I total(I q_len) const {
+    const I nqb = (q_len + 127) / 128;
+    return nqb == 0 ? 0 : offset(nqb - 1) + kvpad;
+  }
+};
+using DeltaRows = DeltaRowsT<int>;
+
+// Entries of one sequence's whole table (host arithmetic).
+inline int64_t delta_seq_len(int causal, int64_t q_len, int64_t kv_len) {
+  return DeltaRowsT<int64_t>(causal, q_len, kv_len).total(q_len);
 }
 
 // Everything a kernel needs, passed by value.
