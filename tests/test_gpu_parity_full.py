@@ -54,3 +54,46 @@ def test_full_size_deterministic():
     run.ws.fill_(0xA5)
     b = run.run()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+ABLATIONS = {"no_k_smooth": 1, "no_q_smooth": 2, "no_smoothing": 3, "per_block_scales": 4}
+
+
+@pytest.mark.parametrize("name", ["mha4k", "prefill8k", "gqa16k", "diffusion32k", "diffusion_varlen"])
+@pytest.mark.parametrize("ablation", list(ABLATIONS))
+def test_full_size_ablation(name, ablation):
+    """Each smoothing / scale-granularity ablation at full size through the GPU path: codes, scales
+    and correction table bit-exact against the oracle's ablation, output to the usual bar, and the
+    accuracy against FP64 equal (to 1e-3) to the oracle's figure recorded for that ablation on the
+    same heads and rows (tests/golden/accuracy_budget.json)."""
+    w = W.WORKLOADS[name]
+    print(f"[ablation-full] {name} {ablation}: start", flush=True)
+    run = H.GpuRun(w, flags=ABLATIONS[ablation])
+    run.run()
+    ws = run.ws_host()
+    budget = {s["b"]: s for s in BUDGET[name]["sequences"]}
+    for b in sorted(budget):
+        rows = np.asarray(budget[b]["rows"], np.int32)
+        info = P.check_sequence(run, b, heads=(w.Hkv - 1, 1), rows=rows, ws=ws, check_s=False,
+                                nthreads=16)
+        want = budget[b]["settings"][ablation]["cos"]
+        print(f"[ablation-full] {name} {ablation} seq {b}: cos_fp64 gpu={info['cos_fp64_gpu']:.4f} "
+              f"oracle={want:.4f} maxerr_fp64 gpu={info['maxerr_fp64_gpu']:.4f} "
+              f"max_abs_vs_oracle={info['max_abs']:.3g}", flush=True)
+        assert abs(info["cos_fp64_gpu"] - want) < 1e-3, (info["cos_fp64_gpu"], want)
+
+
+def test_full_size_single_level_ablation():
+    """The single-level accumulation ablation (no FP32 fold) at the benchmark's workload, held to
+    its own model (the oracle's single-level form plus its per-step error band)."""
+    w = W.WORKLOADS["gqa16k"]
+    run = H.GpuRun(w, flags=8, out_dtype=torch.float32)
+    run.run()
+    rows = np.asarray(BUDGET["gqa16k"]["sequences"][0]["rows"], np.int32)
+    info = P.check_sequence(run, 0, heads=(w.Hkv - 1, 1), rows=rows, check_s=False, nthreads=16)
+    two = H.GpuRun(w, out_dtype=torch.float32)
+    two.run()
+    d = (run.o - two.o).abs().max().item()
+    print(f"[ablation-full] gqa16k no_fp32_fold: band_max={info['single_level_band_max']:.3g} "
+          f"max_abs_vs_model={info['max_abs']:.3g} max|single - two-level| (GPU, all rows)={d:.3g}",
+          flush=True)
