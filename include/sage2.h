@@ -138,29 +138,49 @@ typedef struct {
       delta;
 } sage2_ws_layout;
 
-/* Workspace bytes needed for `p` (validates p first). `bytes` is host memory. */
+/* Workspace bytes needed for `p` (validates p first; the same checks as every call below).
+ * `bytes` is host memory. The workspace holds what the pre-pass produces (see sage2_ws_layout);
+ * its size follows from the envelope of visual companion "SageAttention2 and Fast Exact INT4
+ * Attention", section "Implementation envelope" (variable lengths, grouped heads, padded head
+ * dims). Errors: SAGE2_ERR_NULL for a null p or bytes, otherwise as the parameter checks. */
 sage2_status sage2_workspace_size(const sage2_params* p, size_t* bytes);
 
-/* Pre-pass: smoothing statistics, INT4 codes and scales for Q and K, FP8 codes and scales for V,
- * and the correction table (abstract: Q,K to INT4, P~,V to FP8, smoothed Q; research record:
- * component 1 and 2). q, k, v: device, in_dtype, layout per the strides. ws: device, 256-byte
- * aligned, ws_bytes >= sage2_workspace_size(p). Overwrites the whole workspace region in use. */
+/* Pre-pass (PMLR vol. 267 page "SageAttention2: Efficient Attention with Thorough Outlier
+ * Smoothing and Per-thread INT4 Quantization", Abstract: Q and K to INT4 at thread granularity, P~
+ * and V to FP8, Q smoothed; research record of the same title, "Three components" (1) and (2);
+ * visual companion, "Channel Outlier Smoothing"): K channel means over the sequence, Q means per
+ * 128-token block, INT4 codes of K - mean (one scale per 16-key group) and Q - block mean (one
+ * scale per token), FP8 codes of V with one scale per channel, and the correction table
+ * (block mean . smoothed key) in base-2 logit units.
+ * q, k, v: device, in_dtype, layout per the strides; read only. ws: device, 256-byte aligned,
+ * ws_bytes >= sage2_workspace_size(p); every buffer of the layout in use is overwritten (nothing
+ * in it needs to be initialised). Errors: SAGE2_ERR_NULL (p, q, k, v or ws null), SAGE2_ERR_ALIGN,
+ * SAGE2_ERR_WORKSPACE, the parameter checks, SAGE2_ERR_HIP if a launch fails; on an error before
+ * the launches nothing is enqueued. */
 sage2_status sage2_quantize_smooth(const sage2_params* p, const void* q, const void* k,
                                    const void* v, void* ws, size_t ws_bytes, void* stream);
 
-/* Attention: INT4 QK^T (exact INT32), dequantization with the per-token and per-group scales plus
- * the correction term, online softmax, FP8 P~V with the two-level FP32 fold, division by the row
- * sum and the V channel scale. ws: a workspace filled by sage2_quantize_smooth with the same p
- * (read only). o: device, out_dtype, layout per o_stride; every valid (token, head) row is written. */
+/* Attention (PMLR vol. 267 page, Abstract: INT4 QK^T, FP8 P~V, two-level accumulation; research
+ * record, "Three components" (3); visual companion, "Numerical Repair Stack": exact INT4
+ * fragments, FP8 value mixing, periodic FP32 foldback): exact INT32 QK^T of the INT4 codes,
+ * dequantization with the per-token and per-group scales plus the correction term, online softmax
+ * in base 2 over 128-key tiles, P~ = e4m3 of the weights scaled so the row max maps to 448, P~V
+ * on the FP8 MFMA accumulated per tile and folded into FP32, division by the row sum and the V
+ * channel scale. ws: a workspace filled by sage2_quantize_smooth with the same p (read only; it
+ * may serve any number of calls). o: device, out_dtype, layout per o_stride; every valid
+ * (token, head) row is written, rows that see no key as zeros. Errors: SAGE2_ERR_NULL (p, ws or
+ * o null), SAGE2_ERR_ALIGN, SAGE2_ERR_WORKSPACE, the parameter checks, SAGE2_ERR_HIP if the
+ * launch fails. */
 sage2_status sage2_attn_fwd(const sage2_params* p, const void* ws, size_t ws_bytes, void* o,
                             void* stream);
 
-/* Static English text for a status code. */
+/* Static English text for a status code (never NULL). */
 const char* sage2_status_string(sage2_status s);
 
 /* ---- test-only exports ------------------------------------------------------------------------ */
 
-/* Workspace layout of p (host struct). */
+/* Workspace layout of p (host struct `out`), for tests that decode the pre-pass outputs into the
+ * canonical arrays of the method's steps. Errors: SAGE2_ERR_NULL, the parameter checks. */
 sage2_status sage2_workspace_layout(const sage2_params* p, sage2_ws_layout* out);
 
 /* The attention kernel itself (sage2_attn_fwd's kernel, two-level form), additionally writing for

@@ -779,3 +779,26 @@ def test_accuracy_budget_reproduces(name):
             assert (st[f"narrow{bits}_two_level"]["maxerr_vs_full"]
                     < st[f"narrow{bits}_single_level"]["maxerr_vs_full"])
 
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa16k", "diffusion32k"])
+def test_softmax_tile_size_reading(name):
+    """The online softmax's key tile is part of the result (P~ is rounded against the running max
+    of the tiles seen so far), so the oracle and the kernel share one: 128 keys. Other tile sizes
+    give other, equally valid roundings: each is within 2^-4 max|v| of the unquantized-P~ result
+    (pin B1), so two of them differ by at most max|v| / 8, and the accuracy against FP64 attention
+    does not depend on the choice (cosines within 1e-4)."""
+    wl = W.WORKLOADS["tiny"] if name == "tiny" else _recipe(name, 1024)
+    q, k, v = _seq(wl)
+    rows = np.arange(0, q.shape[1], 5, dtype=np.int32)
+    z = O.quantize(q, k, v)
+    exact = O.attn_fp64(q, k, v, wl.causal, rows=rows)
+    ref, _ = O.attn_quant(z, wl.causal, rows=rows)
+    vmax = float((_dec_table()[z.v8] * z.sv[:, None, :]).max())
+    for bn in (32, 64, 256):
+        out, _ = O.attn_quant(z, wl.causal, rows=rows, bn=bn)
+        d = float(np.abs(out - ref).max())
+        print(f"[R11] {name}: tile {bn} vs 128: max |diff| {d:.4f}, cos vs FP64 {_cos(out, exact):.5f} "
+              f"vs {_cos(ref, exact):.5f}")
+        assert d <= vmax / 8
+        assert abs(_cos(out, exact) - _cos(ref, exact)) < 1e-4
