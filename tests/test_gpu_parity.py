@@ -263,3 +263,47 @@ def _e4m3(c):
         return float("nan")
     return s * (m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
 
+
+
+def test_nonfinite_inputs_complete():
+    """NaN and Inf inputs give unspecified outputs but must not crash: no address in any kernel
+    depends on data values. Every statistic is per (sequence, kv head), so the heads that received
+    no non-finite value produce bit-identical outputs to a clean run."""
+    w = W.custom(2, 4, 2, 300, 300, 128, torch.bfloat16, True, seed=81)
+
+    def poison(q, k, v):
+        q[0, 5, 1, 3] = float("nan")       # batch 0, q head 1 (kv head 0)
+        k[0, 200, 0, 7] = float("inf")     # batch 0, kv head 0
+        v[1, 17, 1, 0] = float("-inf")     # batch 1, kv head 1
+        q[1, 250, 2, :] = float("inf")     # batch 1, q head 2 (kv head 1)
+
+    bad = H.GpuRun(w, modify=poison)
+    bad.run()
+    clean = H.GpuRun(w)
+    clean.run()
+    as_bits = lambda t: t.view(torch.int16)
+    assert torch.equal(as_bits(bad.o[0, :, 2:4]), as_bits(clean.o[0, :, 2:4]))  # batch 0, kv head 1
+    assert torch.equal(as_bits(bad.o[1, :, 0:2]), as_bits(clean.o[1, :, 0:2]))  # batch 1, kv head 0
+
+
+def test_device_seqlens_disagreeing_with_host_copies():
+    """Device cu_seqlens that disagree with the host copies the workspace was sized from (here a
+    second sequence longer than the stated maximum): the plan kernel treats that sequence as empty,
+    so no kernel reads or writes past the workspace or the inputs; its output rows stay untouched
+    and the other sequence is still correct."""
+    import quantized_exact_attention_token_amd as sage2
+    lens = [100, 100]
+    w = W.custom(2, 4, 2, 100, 100, 64, torch.float16, False, seed=82, seqlens=lens)
+    run = H.GpuRun(w)
+    ref = run.run().clone()
+    bad_cu = torch.tensor([0, 100, 5000], dtype=torch.int32, device="cuda")
+    p = sage2.make_params(run.q, run.k, run.v, run.o, False, cu_seqlens_q=run.cu,
+                          cu_seqlens_kv=run.cu_kv, max_seqlen_q=100, max_seqlen_kv=100)
+    p.cu_seqlens_q = bad_cu.data_ptr()      # device copy only; host copies stay [0, 100, 200]
+    p.cu_seqlens_kv = bad_cu.data_ptr()
+    run.o.fill_(float("nan"))
+    sage2.quantize_smooth(p, run.q, run.k, run.v, run.ws)
+    sage2.attn_fwd(p, run.ws, run.o)
+    torch.cuda.synchronize()
+    assert torch.equal(run.o[:100].view(torch.int16), ref[:100].view(torch.int16))
+    assert torch.isnan(run.o[100:].float()).all()
