@@ -216,6 +216,10 @@ def main():
                     help="instead of the benchmark line: time sage2_attn_fwd on the d=128 length "
                          "sweep (N = 4K..32K, causal and not) and print one JSON line with a row "
                          "per configuration")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="instead of the benchmark line: every workload of the measurement plan with "
+                         "step, attention and pre-pass times, the pre-pass share of the step and the "
+                         "workspace bytes, one JSON line with a row per workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel whose HBM counters scale the attention kernel's)")
@@ -241,6 +245,45 @@ def main():
             torch.mul(src, 1, out=dst)  # an elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.all_workloads:
+        rows = []
+        for name in ("tiny", "mha4k", "prefill8k", "gqa16k", "diffusion32k", "diffusion_varlen"):
+            w = W.WORKLOADS[name]
+            run = H.GpuRun(w)
+            stream = torch.cuda.current_stream()
+            t_w = time.perf_counter()
+            n_w = 0
+            while n_w < max(1, args.warmup) or time.perf_counter() - t_w < 0.3:
+                run.prepass()
+                run.attn()
+                n_w += 1
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+            t0 = time.perf_counter()
+            for e in ev:
+                e[0].record(stream)
+                run.prepass()
+                e[1].record(stream)
+                run.attn()
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+            pre = sum(a.elapsed_time(b) for a, b, _ in ev) / len(ev)
+            att = sum(b.elapsed_time(c) for _, b, c in ev) / len(ev)
+            ops = w.attention_ops()
+            rows.append({"workload": name, "step_ms": step_ms, "step_tops": ops / (step_ms * 1e-3) / 1e12,
+                         "attn_ms": att, "kernel_tops": ops / (att * 1e-3) / 1e12,
+                         "frac_of_i8_fp8_peak": ops / (att * 1e-3) / 1e12 / PEAK_TOPS,
+                         "frac_of_mixed_peak": ops / (att * 1e-3) / 1e12 / PEAK_MIXED_TOPS,
+                         "prepass_ms": pre, "prepass_share_of_step": pre / (pre + att),
+                         "workspace_bytes": int(run.ws.numel())})
+            print(f"[all] {name}: step {step_ms:.3f} ms, attention {rows[-1]['kernel_tops']:.0f} TOPS, "
+                  f"pre-pass {pre:.3f} ms", file=sys.stderr, flush=True)
+            del run
+            torch.cuda.empty_cache()
+        print(json.dumps({"metric": METRIC, "unit": "TOPS", "steps": args.steps, "workloads": rows}),
+              flush=True)
         return
     if args.sweep:
         rows = []
@@ -273,6 +316,7 @@ def main():
             rows.append({"workload": name, "N": w.Nq, "causal": w.causal, "attn_ms": avg,
                          "attn_ms_min": ms[0], "kernel_tops": ops / (avg * 1e-3) / 1e12,
                          "frac_of_peak": ops / (avg * 1e-3) / 1e12 / PEAK_TOPS,
+                         "frac_of_mixed_peak": ops / (avg * 1e-3) / 1e12 / PEAK_MIXED_TOPS,
                          "prepass_ms": pre[0].elapsed_time(pre[1])})
             print(f"[sweep] {name}: {rows[-1]['kernel_tops']:.0f} TOPS", file=sys.stderr, flush=True)
             del run
