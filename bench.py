@@ -38,7 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_gqa16k_traffic.json")
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("attn.hip", "device_common.h"):
+    for f in ("attn.hip", "device_common.h", "sage2_internal.h"):
         with open(os.path.join(ROOT, "quantized_exact_attention_token_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
