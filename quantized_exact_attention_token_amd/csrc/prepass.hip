@@ -519,6 +519,7 @@ struct DeltaItem {
   float* delta;
   float L;
   int t, g, grp, qbmin, nlive, koff, li, lk;
+  int grp_log2;  // log2(grp) when grp is a power of two, else -1
 };
 
 // Correction values of 32 pairs (from p0) x 32 NKB keys (from key k0 of the tile): NKB f32 MFMA
@@ -562,19 +563,48 @@ __device__ inline void delta_item(const DeltaItem& c, int p0, int k0) {
   }
   // D[i][j] in register r of lane l: pair p0 + 8 (r / 4) + 4 (l / 32) + r % 4, key
   // t*64 + k0 + 32 kb + l % 32. One store instruction writes two pairs' 32 consecutive keys.
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int pair = p0 + 8 * (r >> 2) + 4 * c.lk + (r & 3);
-    if (pair >= c.nlive) continue;
-    const int h = c.g * c.grp + pair % c.grp, qb = c.qbmin + pair / c.grp;
-    // last key that any row of Q block qb sees
+  const int j0 = c.t * kKVTile + k0 + c.li;
+  const int64_t dl = c.a.lay.delta_len;
+  // last key that any row of Q block qb sees
+  auto last_key = [&](int qb) __attribute__((always_inline)) {
     int jm = c.s.kv_len - 1;
     if (c.a.causal) jm = min(jm, min(c.s.q_len, (qb + 1) * kQBlock) - 1 + c.koff);
-    float* drow = c.delta + (int64_t)h * c.a.lay.delta_len + c.s.delta0 + c.rows.offset(qb);
+    return jm;
+  };
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int j = c.t * kKVTile + k0 + 32 * kb + c.li;
-      drow[j] = j <= jm ? acc[kb][r] * c.L : 0.0f;
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int pb = p0 + 8 * r4 + 4 * c.lk;  // pair of register 4 r4 (a multiple of 4)
+    if (c.grp_log2 >= 2) {
+      // grp a power of two >= 4: pairs pb .. pb + 3 are four consecutive q heads of one Q block
+      // (and nlive, a multiple of grp, covers all four or none), so the row offset and the last
+      // visible key are computed once for the four registers
+      if (pb >= c.nlive) continue;
+      const int qb = c.qbmin + (pb >> c.grp_log2);
+      const int jm = last_key(qb);
+      float* drow = c.delta + (int64_t)(c.g * c.grp + (pb & (c.grp - 1))) * dl + c.s.delta0 +
+                    c.rows.offset(qb);
+#pragma unroll
+      for (int r1 = 0; r1 < 4; ++r1)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int j = j0 + 32 * kb;
+          drow[r1 * dl + j] = j <= jm ? acc[kb][4 * r4 + r1] * c.L : 0.0f;
+        }
+    } else {
+#pragma unroll
+      for (int r1 = 0; r1 < 4; ++r1) {
+        const int pair = pb + r1;
+        if (pair >= c.nlive) continue;
+        const int pq = c.grp_log2 >= 0 ? pair >> c.grp_log2 : pair / c.grp;
+        const int h = c.g * c.grp + (pair - pq * c.grp), qb = c.qbmin + pq;
+        const int jm = last_key(qb);
+        float* drow = c.delta + (int64_t)h * dl + c.s.delta0 + c.rows.offset(qb);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int j = j0 + 32 * kb;
+          drow[j] = j <= jm ? acc[kb][4 * r4 + r1] * c.L : 0.0f;
+        }
+      }
     }
   }
 }
@@ -638,8 +668,9 @@ __device__ inline void delta_tile(const KArgs& a, int t, int g, int b, float* kt
   // splits each block's keys in two halves instead, so that up to twice as many waves have work
   const int nlive = (nqb - qbmin) * grp;
   const int nblk = (nlive + 31) / 32;
+  const int grp_log2 = (grp & (grp - 1)) == 0 ? __builtin_ctz(grp) : -1;
   const DeltaItem it{a, s, kt, DeltaRows(a.causal, s.q_len, s.kv_len), qbar, delta, a.L, t, g, grp,
-                     qbmin, nlive, koff, li, lk};
+                     qbmin, nlive, koff, li, lk, grp_log2};
   if (nblk >= 4) {
     for (int w = wave; w < nblk; w += 4) delta_item<D, 2>(it, 32 * w, 0);
   } else {

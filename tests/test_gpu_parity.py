@@ -60,6 +60,8 @@ EDGE = [
     (2, 4, 2, 200, 333, 64, torch.float16, True),    # Nq < Nkv, bottom-right causal
     (1, 4, 2, 333, 200, 128, torch.bfloat16, True),  # Nq > Nkv: leading rows see no key
     (1, 2, 2, 300, 77, 64, torch.float16, False),
+    (1, 6, 2, 300, 300, 128, torch.bfloat16, True),  # 3 q heads per kv head (not a power of two)
+    (1, 6, 1, 257, 257, 64, torch.float16, True),    # 6 q heads per kv head
 ]
 
 
