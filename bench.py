@@ -107,7 +107,7 @@ def cpu_baseline(run, w, budget_s: float = 20.0):
     import gpu_harness as H
 
     host_cpus = os.cpu_count() or 1
-    threads = min(host_cpus, 16)  # the GPU machine gives one GPU's job a 16-CPU share
+    threads = min(host_cpus, 16)  # a one-GPU job gets a 16-CPU share of the host
     grp = w.Hq // w.Hkv
     import torch
     out = run.out_seq(0)
@@ -225,8 +225,8 @@ def main():
                          "reference kernel whose HBM counters scale the attention kernel's)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the multi-GPU "
-              "sharding of this path is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU only (asked for {args.gpus}); sharding it over "
+              "several GPUs is designed but not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -250,7 +250,7 @@ def main():
         rows = []
         for name in ("tiny", "mha4k", "prefill8k", "gqa16k", "diffusion32k", "diffusion_varlen"):
             w = W.WORKLOADS[name]
-            run = H.GpuRun(w)
+            run = H.DeviceRun(w)
             stream = torch.cuda.current_stream()
             t_w = time.perf_counter()
             n_w = 0
@@ -288,7 +288,7 @@ def main():
     if args.sweep:
         rows = []
         for name, w in W.SWEEP.items():
-            run = H.GpuRun(w)
+            run = H.DeviceRun(w)
             run.prepass()
             # warm-up: at least --warmup calls and at least 0.3 s of back-to-back calls
             t_w = time.perf_counter()
@@ -325,7 +325,7 @@ def main():
                           "steps": args.steps, "sweep": rows}), flush=True)
         return
     w = (W.WORKLOADS | W.SWEEP)[args.workload]
-    run = H.GpuRun(w)
+    run = H.DeviceRun(w)
     stream = torch.cuda.current_stream()
     print(f"[bench] {w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} N{w.Nq} d{w.d} causal={w.causal} "
           f"workspace {run.ws.numel() / 2**20:.0f} MiB", file=sys.stderr, flush=True)

@@ -15,7 +15,7 @@ from quantized_exact_attention_token_amd import workloads as W
 OUT_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
 
 
-class GpuRun:
+class DeviceRun:
     """Inputs on the device, params, workspace, output."""
 
     def __init__(self, w: W.Workload, out_dtype=None, layout: str = "bnhd", device="cuda",

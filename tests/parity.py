@@ -19,7 +19,7 @@ def _eq(name, gpu, ref):
                              f"gpu {gpu[tuple(diff[0])]} oracle {ref[tuple(diff[0])]}")
 
 
-def check_sequence(run: H.GpuRun, b: int, heads=None, rows=None, ws=None, check_s=True,
+def check_sequence(run: H.DeviceRun, b: int, heads=None, rows=None, ws=None, check_s=True,
                    nthreads=0, extra_outputs=None):
     """Bit-exact pre-pass outputs and INT32 QK^T, tolerance-checked attention output, for sequence
     b and the kv-head range `heads` = (first, count) (all heads when None), on query rows `rows`

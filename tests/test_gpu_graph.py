@@ -39,7 +39,7 @@ def _eager(run, q, k, v):
 def test_graph_replays_equal_eager_runs(name):
     w = CASES[name]
     print(f"[graph] {name}: start", flush=True)
-    run = H.GpuRun(w)
+    run = H.DeviceRun(w)
     # warm-up on a side stream before capture (library and torch state settled)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

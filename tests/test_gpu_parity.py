@@ -23,7 +23,7 @@ def _report(name, info):
 
 
 def _full_check(w, out_dtype=None, layout="bnhd", flags=0, sm_scale=0.0, modify=None):
-    run = H.GpuRun(w, out_dtype=out_dtype, layout=layout, flags=flags, sm_scale=sm_scale,
+    run = H.DeviceRun(w, out_dtype=out_dtype, layout=layout, flags=flags, sm_scale=sm_scale,
                    modify=modify)
     run.run()
     ws = run.ws_host()
@@ -41,7 +41,7 @@ def test_tiny_all_outputs(out):
 
 
 def test_tiny_deterministic():
-    run = H.GpuRun(W.WORKLOADS["tiny"])
+    run = H.DeviceRun(W.WORKLOADS["tiny"])
     a = run.run().clone()
     run.o.fill_(0)
     b = run.run()
@@ -110,7 +110,7 @@ def test_varlen_equals_separate_calls():
     """E1: a packed variable-length batch gives bit-identical outputs to one call per sequence."""
     lens = [100, 257, 64]
     w = W.custom(3, 4, 4, 257, 257, 64, torch.float16, True, seed=9, seqlens=lens)
-    run = H.GpuRun(w)
+    run = H.DeviceRun(w)
     packed = run.run().clone()
     cu = run.cu_cpu
     for i, L in enumerate(lens):
@@ -279,9 +279,9 @@ def test_nonfinite_inputs_complete():
         v[1, 17, 1, 0] = float("-inf")     # batch 1, kv head 1
         q[1, 250, 2, :] = float("inf")     # batch 1, q head 2 (kv head 1)
 
-    bad = H.GpuRun(w, modify=poison)
+    bad = H.DeviceRun(w, modify=poison)
     bad.run()
-    clean = H.GpuRun(w)
+    clean = H.DeviceRun(w)
     clean.run()
     as_bits = lambda t: t.view(torch.int16)
     assert torch.equal(as_bits(bad.o[0, :, 2:4]), as_bits(clean.o[0, :, 2:4]))  # batch 0, kv head 1
@@ -296,7 +296,7 @@ def test_device_seqlens_disagreeing_with_host_copies():
     import quantized_exact_attention_token_amd as sage2
     lens = [100, 100]
     w = W.custom(2, 4, 2, 100, 100, 64, torch.float16, False, seed=82, seqlens=lens)
-    run = H.GpuRun(w)
+    run = H.DeviceRun(w)
     ref = run.run().clone()
     bad_cu = torch.tensor([0, 100, 5000], dtype=torch.int32, device="cuda")
     p = sage2.make_params(run.q, run.k, run.v, run.o, False, cu_seqlens_q=run.cu,

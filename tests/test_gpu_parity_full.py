@@ -29,7 +29,7 @@ with open(os.path.join(os.path.dirname(__file__), "golden", "accuracy_budget.jso
 def test_full_size(name):
     w = W.WORKLOADS[name]
     print(f"[parity-full] {name}: start", flush=True)
-    run = H.GpuRun(w)
+    run = H.DeviceRun(w)
     run.run()
     o32 = run.attn_as(torch.float32)
     ws = run.ws_host()
@@ -48,7 +48,7 @@ def test_full_size(name):
 def test_full_size_deterministic():
     """The whole path at the benchmark's workload (gqa16k) twice: bit-identical outputs."""
     w = W.WORKLOADS["gqa16k"]
-    run = H.GpuRun(w)
+    run = H.DeviceRun(w)
     a = run.run().clone()
     run.o.fill_(0)
     run.ws.fill_(0xA5)
@@ -68,7 +68,7 @@ def test_full_size_ablation(name, ablation):
     same heads and rows (tests/golden/accuracy_budget.json)."""
     w = W.WORKLOADS[name]
     print(f"[ablation-full] {name} {ablation}: start", flush=True)
-    run = H.GpuRun(w, flags=ABLATIONS[ablation])
+    run = H.DeviceRun(w, flags=ABLATIONS[ablation])
     run.run()
     ws = run.ws_host()
     budget = {s["b"]: s for s in BUDGET[name]["sequences"]}
@@ -87,11 +87,11 @@ def test_full_size_single_level_ablation():
     """The single-level accumulation ablation (no FP32 fold) at the benchmark's workload, held to
     its own model (the oracle's single-level form plus its per-step error band)."""
     w = W.WORKLOADS["gqa16k"]
-    run = H.GpuRun(w, flags=8, out_dtype=torch.float32)
+    run = H.DeviceRun(w, flags=8, out_dtype=torch.float32)
     run.run()
     rows = np.asarray(BUDGET["gqa16k"]["sequences"][0]["rows"], np.int32)
     info = P.check_sequence(run, 0, heads=(w.Hkv - 1, 1), rows=rows, check_s=False, nthreads=16)
-    two = H.GpuRun(w, out_dtype=torch.float32)
+    two = H.DeviceRun(w, out_dtype=torch.float32)
     two.run()
     d = (run.o - two.o).abs().max().item()
     print(f"[ablation-full] gqa16k no_fp32_fold: band_max={info['single_level_band_max']:.3g} "
@@ -107,7 +107,7 @@ def test_long_sequence():
     w = W.Workload("long64k", 1, 4, 1, 65536, 65536, 128, torch.bfloat16, True, 1200,
                    k_offset_std=4.0, q_offset_std=4.0, n_outliers=4, outlier_scale=20.0)
     print("[parity-full] long64k: start", flush=True)
-    run = H.GpuRun(w)
+    run = H.DeviceRun(w)
     run.run()
     o32 = run.attn_as(torch.float32)
     n = w.Nq
