@@ -209,4 +209,9 @@ def attention(q, k, v, causal: bool = False, sm_scale: float = 0.0, out_dtype=No
     ws = torch.empty(workspace_size(p), dtype=torch.uint8, device=q.device)
     quantize_smooth(p, q, k, v, ws, stream)
     attn_fwd(p, ws, o, stream)
+    if stream is not None:
+        # the kernels may still be reading the workspace (and writing o) on `stream` after this
+        # returns: keep torch's allocator from handing their memory out on another stream meanwhile
+        ws.record_stream(stream)
+        o.record_stream(stream)
     return o

@@ -309,3 +309,22 @@ def test_device_seqlens_disagreeing_with_host_copies():
     torch.cuda.synchronize()
     assert torch.equal(run.o[:100].view(torch.int16), ref[:100].view(torch.int16))
     assert torch.isnan(run.o[100:].float()).all()
+
+
+def test_attention_on_a_side_stream():
+    """The convenience call on a stream other than torch's current one: its workspace is freed on
+    return while the kernels may still run, so it must stay reserved for that stream. Allocations
+    and writes on the current stream right after the call must not disturb the result."""
+    import quantized_exact_attention_token_amd as sage2
+    w = W.custom(1, 8, 2, 1000, 1000, 128, torch.bfloat16, True, seed=91, n_outliers=2,
+                 outlier_scale=20.0, k_offset_std=4.0)
+    run = H.DeviceRun(w)
+    ref = run.run().clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o = sage2.attention(run.q, run.k, run.v, causal=True, stream=side)
+    junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device="cuda") for _ in range(16)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+    del junk
