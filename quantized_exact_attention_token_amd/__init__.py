@@ -122,9 +122,29 @@ def make_params(q, k, v, o=None, causal: bool = False, sm_scale: float = 0.0,
     p = Params()
     p.flags = int(flags)
     varlen = cu_seqlens_q is not None
+    # The library takes raw device pointers and cannot tell what they point to: a host tensor, a
+    # tensor on another device or a mismatched dtype would be read as if it were right.
+    named = [("q", q), ("k", k), ("v", v)] + ([("o", o)] if o is not None else [])
+    if varlen:
+        named += [("cu_seqlens_q", cu_seqlens_q)] + (
+            [("cu_seqlens_kv", cu_seqlens_kv)] if cu_seqlens_kv is not None else [])
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"q, k and v must share one dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
+    if tuple(k.shape) != tuple(v.shape) or k.dim() != q.dim() or k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"shapes do not fit: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if q.dim() != (3 if varlen else 4):
+        raise ValueError("q must be [B, N, H, d], or [tokens, H, d] with cu_seqlens")
+    if o is not None and tuple(o.shape) != tuple(q.shape):
+        raise ValueError(f"o must have q's shape {tuple(q.shape)}, not {tuple(o.shape)}")
+    for name, t in named:
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be on q's device ({q.device}), not {t.device}")
     if varlen:
         if cu_seqlens_kv is None:
             raise ValueError("cu_seqlens_kv is required with cu_seqlens_q")
+        for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+            if c.dtype != torch_int32() or c.dim() != 1 or not c.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
         hq, hkv = q.shape[1], k.shape[1]
         cq_host = cu_seqlens_q.to("cpu", torch_int32()).contiguous()
         ck_host = cu_seqlens_kv.to("cpu", torch_int32()).contiguous()

@@ -228,3 +228,23 @@ def test_causal_correction_rows_match_a_plain_loop(lib):
         want = sum(sum(H.delta_row_keys(bool(causal), a, b)) for a, b in zip(lq, lk))
         assert lay.delta_len == want, (causal, lq, lk, lay.delta_len, want)
 
+
+
+def test_binding_rejects_what_the_library_cannot_check():
+    """The C ABI takes raw device pointers; the binding refuses host tensors, mixed dtypes and
+    mismatched shapes before any pointer reaches the library (no GPU needed to check this)."""
+    import torch
+    q = torch.zeros(1, 16, 4, 64, dtype=torch.float16)
+    k = torch.zeros(1, 16, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="dtype"):
+        sage2.make_params(q, k.to(torch.bfloat16), k, causal=True)
+    with pytest.raises(ValueError, match="shapes"):
+        sage2.make_params(q, k, k[:, :8], causal=True)
+    with pytest.raises(ValueError, match="o must have"):
+        sage2.make_params(q, k, k, o=q[:, :8], causal=True)
+    with pytest.raises(ValueError, match="device"):
+        sage2.make_params(q, k, k, causal=True)       # host tensors
+    with pytest.raises(ValueError, match="device"):
+        sage2.make_params(q[0], k[0], k[0], causal=False,
+                          cu_seqlens_q=torch.tensor([0, 16], dtype=torch.int32),
+                          cu_seqlens_kv=torch.tensor([0, 16], dtype=torch.int32))
