@@ -6,6 +6,8 @@ kernel's arithmetic error of an FP8 boundary, plus half an ulp of the output for
 >= 0.9999 against the oracle's quantized pipeline. Accuracy against FP64 attention is recorded
 and must match the oracle's own to within 1e-3 (the GPU path is as accurate as the method).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -205,6 +207,40 @@ def test_random_configurations(seed):
     split their grids by role, so shapes that leave some roles empty are included)."""
     w = _random_case(seed)
     print(f"[parity] random {seed}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Nq{w.Nq} Nkv{w.Nkv} d{w.d} "
+          f"{str(w.dtype).split('.')[-1]} causal={w.causal} seqlens={w.seqlens}", flush=True)
+    _full_check(w)
+
+
+# Wider mixed configurations: GQA groups of 1 to 8 q heads per kv head (3 and 6 included), up to
+# 1500 tokens (many key tiles, ragged tails), outlier and offset strengths varied. A handful run by
+# default; SAGE2_WIDE_CASES=N runs N of them.
+_WIDE_CASES = int(os.environ.get("SAGE2_WIDE_CASES", "16"))
+
+
+def _wide_case(seed):
+    rng = np.random.default_rng(50000 + seed)
+    hkv = int(rng.choice([1, 2, 3]))
+    hq = hkv * int(rng.choice([1, 2, 3, 4, 6, 8]))
+    d = 8 * int(rng.integers(1, 17))
+    dt = torch.float16 if rng.integers(2) else torch.bfloat16
+    causal = bool(rng.integers(2))
+    kw = dict(n_outliers=int(rng.integers(0, 3)), outlier_scale=float(rng.choice([5.0, 20.0])),
+              k_offset_std=float(rng.choice([0.0, 4.0])))
+    if rng.integers(2):
+        lens = [int(x) for x in rng.integers(0, 1500, size=int(rng.integers(1, 4)))]
+        if max(lens) == 0:
+            lens[0] = 1
+        n = max(lens)
+        return W.custom(len(lens), hq, hkv, n, n, d, dt, causal, seed=seed, seqlens=lens, **kw)
+    b = int(rng.integers(1, 3))
+    nq, nkv = int(rng.integers(1, 1500)), int(rng.integers(1, 1500))
+    return W.custom(b, hq, hkv, nq, nkv, d, dt, causal, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(_WIDE_CASES))
+def test_wide_random_configurations(seed):
+    w = _wide_case(seed)
+    print(f"[parity] wide {seed}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Nq{w.Nq} Nkv{w.Nkv} d{w.d} "
           f"{str(w.dtype).split('.')[-1]} causal={w.causal} seqlens={w.seqlens}", flush=True)
     _full_check(w)
 
